@@ -1,0 +1,289 @@
+/*
+ * oracle.c -- plain, slow CPU oracle for exact Gumbel-Max sampling fused into
+ * the LM-head matmul ("FlashSampling: Fast and Memory-Efficient Exact
+ * Sampling").
+ *
+ * TEST INFRASTRUCTURE ONLY.  Only the test-suite, the smoke check and the
+ * benchmark's CPU-baseline leg may load this library.  The GPU product path
+ * never calls it and shares no source with it: the Philox generator, the
+ * uniform/Gumbel maps, the logits and the comparator below are written here
+ * a second time, independently of the HIP kernels.
+ *
+ * What it computes is the plain definition the method is proved to reach
+ * exactly (wiki summary page, "Key claims": argmax over logits plus Gumbel
+ * noise decomposes over any partition of the vocabulary, so the tiled kernel
+ * returns the same maximiser as one global argmax; arXiv abstract page: the
+ * sampler is exact, not approximate):
+ *
+ *   1. full logits  z[b][v] = sum_d h[b][d] * W[v][d]            (no bias)
+ *   2. scaled score s = z * (1/T[b])   (wiki summary, "Method", step 3 of
+ *      the four-op decode step: temperature scaling)
+ *   3. perturbed    s += g,  g = -log(-log u),  u from a counter-based
+ *      generator keyed on (seed, step, row, global vocab index) -- the pages
+ *      say only that each element of the tile gets its own Gumbel draw from
+ *      the tile's RNG state ("Method"); the generator is Philox-4x32-10
+ *      (Salmon, Moraes, Dror, Shaw, "Parallel random numbers: as easy as
+ *      1, 2, 3", SC'11)
+ *   4. one global argmax per row; ties go to the smaller global index.
+ *
+ * Precision: every dot product is summed in fp64 (bf16 -> fp64 is exact, each
+ * product is exact) in increasing d and rounded once to fp32; the Gumbel
+ * value is evaluated in fp64 and rounded once to fp32; the temperature scale
+ * and the noise add are separate fp32 operations (compile with
+ * -ffp-contract=off so that no fused multiply-add is formed).
+ *
+ * Parallelism: OpenMP over independent outputs only (rows or seeds); no
+ * output depends on the thread count or the schedule.
+ */
+#include <math.h>
+#include <stddef.h>
+#include <stdint.h>
+#include <string.h>
+
+#define ORACLE_EXPORT __attribute__((visibility("default")))
+
+/* ---------------------------------------------------------------------- */
+/* Philox-4x32-10 (SC'11 paper, section 5: the Philox round is two 32x32->64
+ * multiplications by fixed odd constants whose halves are permuted and xored
+ * with the other counter words and the round key; the key is bumped by the
+ * Weyl increments between rounds).                                         */
+/* ---------------------------------------------------------------------- */
+static const uint32_t PHILOX_MUL_A = 0xD2511F53u; /* multiplies word 0 */
+static const uint32_t PHILOX_MUL_B = 0xCD9E8D57u; /* multiplies word 2 */
+static const uint32_t PHILOX_WEYL_0 = 0x9E3779B9u; /* golden ratio */
+static const uint32_t PHILOX_WEYL_1 = 0xBB67AE85u; /* sqrt(3) - 1 */
+
+ORACLE_EXPORT void oracle_philox4x32_10(const uint32_t ctr_in[4],
+                                        const uint32_t key_in[2],
+                                        uint32_t out[4]) {
+  uint32_t c0 = ctr_in[0], c1 = ctr_in[1], c2 = ctr_in[2], c3 = ctr_in[3];
+  uint32_t k0 = key_in[0], k1 = key_in[1];
+  for (int round = 0; round < 10; ++round) {
+    if (round > 0) { /* key schedule: bump before every round but the first */
+      k0 += PHILOX_WEYL_0;
+      k1 += PHILOX_WEYL_1;
+    }
+    uint64_t prod_a = (uint64_t)PHILOX_MUL_A * (uint64_t)c0;
+    uint64_t prod_b = (uint64_t)PHILOX_MUL_B * (uint64_t)c2;
+    uint32_t hi_a = (uint32_t)(prod_a >> 32), lo_a = (uint32_t)prod_a;
+    uint32_t hi_b = (uint32_t)(prod_b >> 32), lo_b = (uint32_t)prod_b;
+    uint32_t n0 = hi_b ^ c1 ^ k0;
+    uint32_t n1 = lo_b;
+    uint32_t n2 = hi_a ^ c3 ^ k1;
+    uint32_t n3 = lo_a;
+    c0 = n0; c1 = n1; c2 = n2; c3 = n3;
+  }
+  out[0] = c0; out[1] = c1; out[2] = c2; out[3] = c3;
+}
+
+/* Raw 32-bit noise word for (seed, step, row, global vocab index gv).
+ * Counter = (gv / 4, row, step low word, step high word); key = (seed low
+ * word, seed high word); the element takes output word gv mod 4, so one
+ * generator call covers four consecutive vocabulary ids.  Keying on the
+ * global index makes the noise field independent of how V is tiled or
+ * sharded (wiki summary, "Method": per-rank shards use the same per-element
+ * draw as an unsharded run).                                               */
+ORACLE_EXPORT uint32_t oracle_noise_bits(uint64_t seed, uint64_t step,
+                                         uint32_t row, uint32_t gv) {
+  uint32_t ctr[4] = {gv >> 2, row, (uint32_t)step, (uint32_t)(step >> 32)};
+  uint32_t key[2] = {(uint32_t)seed, (uint32_t)(seed >> 32)};
+  uint32_t out[4];
+  oracle_philox4x32_10(ctr, key, out);
+  return out[gv & 3u];
+}
+
+/* Uniform in the open interval (0,1): the top 23 bits k of the word give the
+ * odd multiple (2k+1) * 2^-24.  Exact in fp32; never 0 or 1, so the Gumbel
+ * value below is always finite.                                            */
+ORACLE_EXPORT float oracle_uniform(uint32_t bits) {
+  uint32_t k = bits >> 9;
+  double u = (double)(2u * k + 1u) * 0x1p-24;
+  return (float)u; /* exact: 2k+1 < 2^24 */
+}
+
+/* Standard Gumbel draw by inversion of its CDF exp(-exp(-g)):
+ * g = -log(-log u), evaluated in fp64 and rounded once to fp32.            */
+ORACLE_EXPORT float oracle_gumbel(uint32_t bits) {
+  double u = (double)oracle_uniform(bits);
+  double g = -log(-log(u));
+  return (float)g;
+}
+
+/* Bulk forms of the three maps above, one output per input element.      */
+ORACLE_EXPORT void oracle_noise_bits_range(uint64_t seed, uint64_t step,
+                                           uint32_t row, uint32_t gv0, int64_t n,
+                                           uint32_t* out) {
+#pragma omp parallel for schedule(static)
+  for (int64_t i = 0; i < n; ++i)
+    out[i] = oracle_noise_bits(seed, step, row, gv0 + (uint32_t)i);
+}
+
+ORACLE_EXPORT void oracle_uniform_array(const uint32_t* bits, int64_t n, float* out) {
+#pragma omp parallel for schedule(static)
+  for (int64_t i = 0; i < n; ++i) out[i] = oracle_uniform(bits[i]);
+}
+
+ORACLE_EXPORT void oracle_gumbel_array(const uint32_t* bits, int64_t n, float* out) {
+#pragma omp parallel for schedule(static)
+  for (int64_t i = 0; i < n; ++i) out[i] = oracle_gumbel(bits[i]);
+}
+
+/* ---------------------------------------------------------------------- */
+/* Logits                                                                   */
+/* ---------------------------------------------------------------------- */
+static double bf16_to_double(uint16_t x) {
+  uint32_t w = (uint32_t)x << 16;
+  float f;
+  memcpy(&f, &w, sizeof f);
+  return (double)f;
+}
+
+/* One logit z = sum_d h[d] * W[d], fp64 in increasing d, rounded once.    */
+ORACLE_EXPORT float oracle_logit(const uint16_t* h_row, const uint16_t* w_row,
+                                 int32_t D) {
+  double acc = 0.0;
+  for (int32_t d = 0; d < D; ++d)
+    acc += bf16_to_double(h_row[d]) * bf16_to_double(w_row[d]);
+  return (float)acc;
+}
+
+/* Full fp32 logits z[b][v] for b < B, v < V (row-major B x V).            */
+ORACLE_EXPORT void oracle_logits(const uint16_t* h, const uint16_t* W,
+                                 int32_t B, int32_t D, int32_t V, float* z) {
+#pragma omp parallel for schedule(dynamic, 1)
+  for (int32_t b = 0; b < B; ++b)
+    for (int32_t v = 0; v < V; ++v)
+      z[(size_t)b * V + v] = oracle_logit(h + (size_t)b * D, W + (size_t)v * D, D);
+}
+
+/* ---------------------------------------------------------------------- */
+/* Scores and the global argmax                                             */
+/* ---------------------------------------------------------------------- */
+/* A row is greedy when its temperature is not a positive number (0, -0,
+ * negative or NaN): the T -> 0 limit of the sampler is the plain argmax of
+ * the logits, so such rows take s = z with no scaling and no noise.       */
+static int is_greedy(float T) { return !(T > 0.0f); }
+
+static float score(float z, float T, float inv_T, uint64_t seed, uint64_t step,
+                   uint32_t row, uint32_t gv) {
+  if (is_greedy(T)) return z;
+  float scaled = z * inv_T;                                 /* fp32 multiply */
+  float g = oracle_gumbel(oracle_noise_bits(seed, step, row, gv));
+  return scaled + g;                                        /* fp32 add */
+}
+
+/* Perturbed score of one element, for checks on a single (row, id).       */
+ORACLE_EXPORT float oracle_score(float z, float T, uint64_t seed, uint64_t step,
+                                 uint32_t row, uint32_t gv) {
+  float inv_T = is_greedy(T) ? 1.0f : 1.0f / T;
+  return score(z, T, inv_T, seed, step, row, gv);
+}
+
+typedef struct {
+  float best;
+  int32_t best_id;
+  float second; /* largest score among the other ids */
+} running_max;
+
+static void rm_init(running_max* r) {
+  r->best = -INFINITY;
+  r->best_id = -1;
+  r->second = -INFINITY;
+}
+
+/* Elements arrive in increasing global id, so a strict '>' keeps the
+ * smaller id on a tie.                                                     */
+static void rm_push(running_max* r, float s, int32_t gv) {
+  if (r->best_id < 0 || s > r->best) {
+    if (r->best_id >= 0) r->second = r->best;
+    r->best = s;
+    r->best_id = gv;
+  } else if (s > r->second) {
+    r->second = s;
+  }
+}
+
+/* Sample the listed rows (rows == NULL: rows 0..n_rows-1) of a decode step.
+ * h is B x D and W is V x D (bf16 bits, row-major); row r of the batch uses
+ * noise key (seed, step, r) and its vocabulary ids are vocab_offset + v.
+ * Outputs per listed row: sampled global id, winning perturbed score, and
+ * the gap between the winner and the runner-up.                            */
+ORACLE_EXPORT void oracle_sample(const uint16_t* h, const uint16_t* W,
+                                 int32_t D, int32_t V, int32_t vocab_offset,
+                                 const float* T, uint64_t seed, uint64_t step,
+                                 const int32_t* rows, int32_t n_rows,
+                                 int32_t* out_id, float* out_val,
+                                 float* out_gap) {
+#pragma omp parallel for schedule(dynamic, 1)
+  for (int32_t i = 0; i < n_rows; ++i) {
+    int32_t b = rows ? rows[i] : i;
+    float Tb = T[b];
+    float inv_T = is_greedy(Tb) ? 1.0f : 1.0f / Tb;
+    running_max r;
+    rm_init(&r);
+    for (int32_t v = 0; v < V; ++v) {
+      float z = oracle_logit(h + (size_t)b * D, W + (size_t)v * D, D);
+      int32_t gv = vocab_offset + v;
+      rm_push(&r, score(z, Tb, inv_T, seed, step, (uint32_t)b, (uint32_t)gv), gv);
+    }
+    out_id[i] = r.best_id;
+    out_val[i] = r.best;
+    out_gap[i] = r.best - r.second;
+  }
+}
+
+/* Same, from precomputed fp32 logits: z is n_rows x V and T has n_rows
+ * entries, one per listed row; rows[i] (or i) is that row's batch position,
+ * which keys its noise.  Repeated for n_seeds consecutive seeds seed0,
+ * seed0+1, ...; output index is [seed][row].  Used for distribution checks,
+ * where the logits stay fixed and only the noise changes.                  */
+ORACLE_EXPORT void oracle_sample_logits(const float* z, int32_t V,
+                                        int32_t vocab_offset, const float* T,
+                                        uint64_t seed0, int32_t n_seeds,
+                                        uint64_t step, const int32_t* rows,
+                                        int32_t n_rows, int32_t* out_id,
+                                        float* out_val, float* out_gap) {
+#pragma omp parallel for schedule(dynamic, 64)
+  for (int64_t job = 0; job < (int64_t)n_seeds * n_rows; ++job) {
+    int32_t si = (int32_t)(job / n_rows), i = (int32_t)(job % n_rows);
+    int32_t b = rows ? rows[i] : i;
+    float Tb = T[i];
+    float inv_T = is_greedy(Tb) ? 1.0f : 1.0f / Tb;
+    uint64_t seed = seed0 + (uint64_t)si;
+    running_max r;
+    rm_init(&r);
+    for (int32_t v = 0; v < V; ++v) {
+      int32_t gv = vocab_offset + v;
+      rm_push(&r, score(z[(size_t)i * V + v], Tb, inv_T, seed, step, (uint32_t)b,
+                        (uint32_t)gv), gv);
+    }
+    out_id[job] = r.best_id;
+    if (out_val) out_val[job] = r.best;
+    if (out_gap) out_gap[job] = r.best - r.second;
+  }
+}
+
+/* ---------------------------------------------------------------------- */
+/* Merge of per-part (max, argmax) pairs                                    */
+/* ---------------------------------------------------------------------- */
+/* Partials are P x B, part-major: (val[p*B + b], id[p*B + b]).  Per row the
+ * winner is the largest value, and among equal values the smallest id:
+ * this is the cross-part argmax that makes per-tile and per-rank maximisers
+ * reproduce the global one (wiki summary, "Method").                        */
+ORACLE_EXPORT void oracle_merge(const float* val, const int32_t* id, int32_t P,
+                                int32_t B, int32_t* out_id, float* out_val) {
+  for (int32_t b = 0; b < B; ++b) {
+    float best = val[b];
+    int32_t best_id = id[b];
+    for (int32_t p = 1; p < P; ++p) {
+      float v = val[(size_t)p * B + b];
+      int32_t i = id[(size_t)p * B + b];
+      if (v > best || (v == best && i < best_id)) {
+        best = v;
+        best_id = i;
+      }
+    }
+    out_id[b] = best_id;
+    out_val[b] = best;
+  }
+}
