@@ -1,0 +1,216 @@
+#!/usr/bin/env python3
+"""Benchmark of the fused LM-head + exact Gumbel-Max sampler on one MI355X.
+
+One step = one fs_sample call (LM-head contraction, temperature scaling,
+Gumbel perturbation, per-tile (max, argmax), merge) over one batch of the
+Llama-3-8B-shaped LM head (D = 4096, V = 128256, bf16), with the inputs
+already resident in device memory and a fresh (seed, step) per step.  The
+headline line is B = 32; the same line carries the B = 1 .. 256 sweep, the
+unfused baseline (logits and probabilities through device memory) timed the
+same way, the fused kernel's roofline fraction and the CPU oracle's rate.
+
+Prints ONE JSON line on stdout.  Usage:
+  python bench.py [--gpus 1] [--steps K] [--warmup W] [--batch 32]
+                  [--sweep 1,2,4,...] [--no-cpu-baseline] [--profile-pass]
+--profile-pass runs a short fixed sequence for rocprofv3 (a few fused steps
+plus a 1 GiB device copy used to calibrate the HBM byte counters) and exits.
+"""
+import argparse
+import json
+import os
+import sys
+import time
+
+ROOT = os.path.dirname(os.path.abspath(__file__))
+if ROOT not in sys.path:
+    sys.path.insert(0, ROOT)
+
+METRIC = "fused LM-head+sample µs/step & % roofline, B=1..256, D=4096, V=128256"
+HBM_PEAK_GBS = 8000.0          # MI355X HBM3E, 8 TB/s
+MFMA_BF16_PEAK_TFLOPS = 2500.0  # MI355X dense bf16 MFMA
+
+
+def parse():
+    ap = argparse.ArgumentParser(description=__doc__.splitlines()[0])
+    ap.add_argument("--gpus", type=int, default=1)
+    ap.add_argument("--steps", type=int, default=200)
+    ap.add_argument("--warmup", type=int, default=20)
+    ap.add_argument("--batch", type=int, default=32)
+    ap.add_argument("--sweep", default="1,2,4,8,16,32,64,128,256")
+    ap.add_argument("--sweep-steps", type=int, default=100)
+    ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--no-unfused", action="store_true")
+    ap.add_argument("--profile-pass", action="store_true")
+    return ap.parse_args()
+
+
+def algorithmic_bytes(B, D, V):
+    """Bytes the fused step must move: W and h read once, T read, one
+    (id, score) pair written per row.  Per-tile partials are implementation
+    traffic (8 bytes per row per tile, under 0.2 % here) and not counted."""
+    return 2 * V * D + 2 * B * D + 4 * B + 8 * B
+
+
+def flops(B, D, V):
+    return 2 * B * V * D
+
+
+def roofline_us(B, D, V):
+    return max(algorithmic_bytes(B, D, V) / (HBM_PEAK_GBS * 1e3),
+               flops(B, D, V) / (MFMA_BF16_PEAK_TFLOPS * 1e6))
+
+
+def time_steps(torch, fn, steps, warmup, stream):
+    """Warm up, then time `steps` calls between two events on `stream`;
+    returns milliseconds per step."""
+    for i in range(warmup):
+        fn(i)
+    torch.cuda.synchronize()
+    start = torch.cuda.Event(enable_timing=True)
+    stop = torch.cuda.Event(enable_timing=True)
+    start.record(stream)
+    for i in range(steps):
+        fn(warmup + i)
+    stop.record(stream)
+    torch.cuda.synchronize()
+    return start.elapsed_time(stop) / steps
+
+
+def measure_fused_kernel(torch, fsl, fn, steps, warmup):
+    """Average duration of the fused kernel alone (HIP events recorded by the
+    library around each launch on the caller's stream)."""
+    for i in range(warmup):
+        fn(i)
+    torch.cuda.synchronize()
+    fsl.profile_enable(steps)
+    for i in range(steps):
+        fn(warmup + i)
+    n, tot, lo, hi = fsl.profile_read()
+    fsl.profile_enable(0)
+    return tot / max(n, 1), lo, hi, n
+
+
+def main():
+    args = parse()
+    if args.gpus != 1:
+        print(f"bench.py measures one GPU only; --gpus {args.gpus} is not supported "
+              "(the sampler runs on one device; see the sharding notes in the design document)",
+              file=sys.stderr)
+        sys.exit(2)
+
+    import torch
+    import lm_head_exact_amd as fsl
+    from lm_head_exact_amd import workloads as wl
+
+    dev = torch.device("cuda:0")
+    torch.cuda.set_device(dev)
+    props = torch.cuda.get_device_properties(dev)
+    wlk = wl.LLAMA3_8B
+    D, V = wlk.D, wlk.V
+    W = wl.make_w(wlk, dev)
+    stream = torch.cuda.current_stream(dev)
+
+    def make_step(B, unfused=False):
+        h = wl.make_h(wlk, B, dev)
+        T = wl.make_temperature(wlk, B, dev)
+        out = (torch.empty(B, dtype=torch.int32, device=dev),
+               torch.empty(B, dtype=torch.float32, device=dev))
+        if unfused:
+            ws = fsl.binding.alloc_workspace(fsl.unfused_workspace_bytes(B, D, V), dev)
+            call = fsl.sample_unfused
+        else:
+            ws = fsl.binding.alloc_workspace(fsl.workspace_bytes(B, D, V), dev)
+            call = fsl.sample
+
+        def fn(i):
+            seed, step = wlk.sampler_seed(i)
+            call(h, W, T, seed, step, out=out, workspace=ws)
+        return fn, (h, T, out, ws)
+
+    if args.profile_pass:
+        fn, keep = make_step(args.batch)
+        for i in range(5):
+            fn(i)
+        torch.cuda.synchronize()
+        src = torch.empty(1 << 30, dtype=torch.uint8, device=dev).fill_(1)
+        dst = torch.empty_like(src)
+        dst.copy_(src)          # 1 GiB read + 1 GiB write: counter calibration
+        torch.cuda.synchronize()
+        print(json.dumps({"profile_pass": True, "B": args.batch, "copy_bytes": 1 << 30}))
+        return
+
+    B = args.batch
+    fn, keep = make_step(B)
+    ms = time_steps(torch, fn, args.steps, args.warmup, stream)
+    k_ms, k_lo, k_hi, k_n = measure_fused_kernel(torch, fsl, fn, args.steps, args.warmup)
+    us = ms * 1e3
+    k_us = k_ms * 1e3
+    bytes_ = algorithmic_bytes(B, D, V)
+    achieved_gbs = bytes_ / (k_us * 1e3)
+    sweep = []
+    for b in [int(x) for x in args.sweep.split(",") if x]:
+        f, kp = make_step(b)
+        t = time_steps(torch, f, args.sweep_steps, 10, stream) * 1e3
+        kt, _, _, _ = measure_fused_kernel(torch, fsl, f, args.sweep_steps, 5)
+        kt *= 1e3
+        entry = {"B": b, "us_per_step": round(t, 2), "kernel_us": round(kt, 2),
+                 "roofline_us": round(roofline_us(b, D, V), 2),
+                 "frac_of_roofline": round(roofline_us(b, D, V) / t, 4),
+                 "kernel_hbm_GBs": round(algorithmic_bytes(b, D, V) / (kt * 1e3), 1),
+                 "kernel_mfma_TFLOPs": round(flops(b, D, V) / (kt * 1e6), 1),
+                 "tokens_per_s": round(b / (t * 1e-6), 1)}
+        if not args.no_unfused:
+            uf, ukp = make_step(b, unfused=True)
+            ut = time_steps(torch, uf, max(10, args.sweep_steps // 4), 3, stream) * 1e3
+            entry["unfused_us_per_step"] = round(ut, 2)
+            entry["unfused_intermediate_bytes"] = 20 * b * V
+            del ukp
+        sweep.append(entry)
+        del kp
+    unf_us = None
+    if not args.no_unfused:
+        uf, ukp = make_step(B, unfused=True)
+        unf_us = time_steps(torch, uf, max(20, args.steps // 4), 5, stream) * 1e3
+        del ukp
+
+    cpu = None
+    if not args.no_cpu_baseline:
+        import oracle
+        h_cpu = wl.bf16_bits(keep[0])
+        T_cpu = keep[1].cpu().numpy()
+        W_cpu = wl.bf16_bits(W)
+        rows = list(range(B))
+        t0 = time.perf_counter()
+        oracle.sample(h_cpu, W_cpu, T_cpu, *wlk.sampler_seed(0), rows=rows)
+        dt = time.perf_counter() - t0
+        cpu = {"value": round(dt * 1e6 * B / len(rows), 1), "unit": "µs/step",
+               "cores": oracle.max_threads(), "kind": "oracle",
+               "sample": f"one full decode step of the B={B} workload (all {len(rows)} rows, "
+                         f"full V={V}, fp64 dot products), {dt:.2f} s wall"}
+
+    line = {
+        "metric": METRIC, "value": round(us, 2), "unit": "µs/step", "n_gpus": 1,
+        "steps": args.steps, "warmup": args.warmup, "ms_per_step": round(ms, 5),
+        "higher_is_better": False, "scaling": "weak", "vs_baseline": None, "dtype": "bf16",
+        "data": "synthetic (seeded N(0,0.02^2) weights, RMS-normalised N(0,1) hidden states)",
+        "config": {"workload": wlk.name, "B": B, "D": D, "V": V, "temperature": 1.0,
+                   "fresh_seed_per_step": True},
+        "tokens_per_s": round(B / (us * 1e-6), 1),
+        "frac_of_roofline": round(roofline_us(B, D, V) / us, 4),
+        "roofline": {"bound": "hbm", "achieved": round(achieved_gbs, 1), "peak": HBM_PEAK_GBS,
+                     "unit": "GB/s", "frac": round(achieved_gbs / HBM_PEAK_GBS, 4),
+                     "traffic": None, "kernel": "fused_sample_kernel",
+                     "kernel_avg_us": round(k_us, 2), "kernel_min_us": round(k_lo * 1e3, 2),
+                     "kernel_max_us": round(k_hi * 1e3, 2), "kernel_launches": k_n,
+                     "algorithmic_bytes_per_launch": bytes_},
+        "unfused_us_per_step": round(unf_us, 2) if unf_us is not None else None,
+        "cpu_baseline": cpu,
+        "sweep": sweep,
+        "device": {"name": props.name, "cus": props.multi_processor_count,
+                   "gcn_arch": getattr(props, "gcnArchName", "")},
+    }
+    print(json.dumps(line), flush=True)
+
+
+if __name__ == "__main__":
+    main()

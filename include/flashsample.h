@@ -1,0 +1,169 @@
+/*
+ * flashsample.h -- C ABI of libflashsample: exact categorical sampling fused
+ * into the LM-head matmul, for AMD Instinct MI355X (gfx950).
+ *
+ * The operation ("FlashSampling: Fast and Memory-Efficient Exact Sampling";
+ * wiki summary page, sections "Key claims" and "Method"; arXiv abstract):
+ * for each batch row b the library draws one token id from
+ * softmax(z_b / T_b), z_b = W h_b, by the Gumbel-Max trick -- the argmax over
+ * v of  s[b][v] = z[b][v] / T_b + g[b][v]  with g standard Gumbel noise.  The
+ * logits are formed tile by tile on chip, scaled, perturbed and reduced to
+ * one (max, argmax) pair per row and per vocabulary tile; a small reduction
+ * over tiles returns the id.  The B x V logits never reach device memory.
+ *
+ * Noise field.  The pages leave the generator open; here it is
+ * Philox-4x32-10 (Salmon et al., SC'11).  For batch row b and GLOBAL
+ * vocabulary id gv = vocab_offset + v:
+ *   x = word (gv mod 4) of Philox4x32_10(counter = {gv / 4, b, step_lo,
+ *       step_hi}, key = {seed_lo, seed_hi})
+ *   u = (2 (x >> 9) + 1) * 2^-24            (exact fp32, 0 < u < 1)
+ *   g = -log(-log u)
+ * Keying on the global id makes the field independent of tiling and of
+ * vocabulary sharding, so per-shard results merge to the unsharded result
+ * (wiki summary, "Method", tensor-parallel paragraph).
+ *
+ * Scores.  s = z * fp32(1/T_b) + g, with z accumulated in fp32 from bf16
+ * products.  A row whose temperature is not a positive number (0, -0,
+ * negative, NaN) is greedy: s = z (no scaling, no noise).  Ties go to the
+ * smaller global id.
+ *
+ * Conventions for every entry point:
+ *   - h is bf16 [B][D] row-major, W is bf16 [V][D] row-major (the layout of
+ *     an nn.Linear weight); both device pointers, 16-byte aligned; D % 8 == 0.
+ *   - temperature, out_ids, out_maxval, partials: device pointers, 4-byte
+ *     aligned.  workspace: device pointer, 256-byte aligned.
+ *   - stream is a hipStream_t (NULL = the default stream).  Calls are
+ *     asynchronous and ordered on that stream; the caller keeps every buffer
+ *     alive until the stream has reached the work.
+ *   - Ownership: the caller owns all memory.  The library allocates nothing,
+ *     keeps no pointer after returning and holds no state between calls
+ *     other than a forced-configuration switch (fs_force_config).
+ *   - Errors: the return code is the only channel.  Arguments are checked on
+ *     the host before any HIP call; a rejected call launches nothing and
+ *     writes nothing.  FS_ERR_HIP carries the runtime's message in
+ *     fs_last_error() (thread-local).  Device-resident values are not
+ *     inspected: NaN or infinite entries in h or W give undefined ids.
+ *   - B == 0 is a no-op that returns FS_OK (pointers may then be NULL).
+ *   - Reentrant: concurrent calls are safe if they use distinct workspaces.
+ */
+#ifndef FLASHSAMPLE_H
+#define FLASHSAMPLE_H
+
+#include <stddef.h>
+#include <stdint.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+#define FS_API __attribute__((visibility("default")))
+
+typedef enum {
+  FS_OK = 0,
+  FS_ERR_INVALID_ARG = 1, /* null/misaligned pointer, bad size or range */
+  FS_ERR_UNSUPPORTED = 2, /* valid request this build cannot run */
+  FS_ERR_WORKSPACE = 3,   /* workspace_bytes below the required size */
+  FS_ERR_HIP = 4          /* a HIP runtime call or launch failed */
+} fs_status;
+
+/* Bytes of workspace fs_sample / fs_sample_partial need for (B, D, V).
+ * Returns 0 when the sizes are invalid (see fs_sample). */
+FS_API size_t fs_workspace_bytes(int32_t B, int32_t D, int32_t V);
+
+/* Bytes of workspace fs_sample_unfused needs: the materialised fp32 logits
+ * and probabilities (2 * B * V * 4 bytes) plus per-row statistics. */
+FS_API size_t fs_unfused_workspace_bytes(int32_t B, int32_t D, int32_t V);
+
+/* Sample one token id per batch row (wiki summary, "Method": per-tile
+ * maximisers over vocabulary tiles, then the partition argmax).
+ *   h            bf16 [B][D]
+ *   W            bf16 [V][D]; row v has global id vocab_offset + v
+ *   B, D, V      B >= 0; D >= 8, D % 8 == 0; V >= 1
+ *   vocab_offset >= 0 and vocab_offset + V <= 2^31 - 1
+ *   temperature  fp32 [B]; !(T > 0) selects greedy for that row
+ *   seed, step   64-bit noise key and step counter (fresh per decode step)
+ *   out_ids      int32 [B]: sampled GLOBAL id per row
+ *   out_maxval   fp32 [B]: the winning perturbed score s
+ *   workspace    >= fs_workspace_bytes(B, D, V) bytes; contents on entry
+ *                are ignored (scratch for per-tile partials)             */
+FS_API fs_status fs_sample(const void* h, const void* W, int32_t B, int32_t D, int32_t V,
+                    int32_t vocab_offset, const float* temperature, uint64_t seed,
+                    uint64_t step, int32_t* out_ids, float* out_maxval,
+                    void* workspace, size_t workspace_bytes, void* stream);
+
+/* One vocabulary shard's contribution for the grouped / tensor-parallel flow
+ * (wiki summary, "Method": each rank reduces its own shard to a per-row
+ * (local max, local argmax) pair, and only those pairs are exchanged).
+ * Same inputs and semantics as fs_sample over rows [vocab_offset,
+ * vocab_offset + V) of the global vocabulary; writes partial_val[b] and
+ * partial_idx[b] (GLOBAL ids), i.e. slot p of a P x B partial buffer when
+ * the caller passes base + p * B. */
+FS_API fs_status fs_sample_partial(const void* h, const void* W, int32_t B, int32_t D,
+                            int32_t V, int32_t vocab_offset, const float* temperature,
+                            uint64_t seed, uint64_t step, float* partial_val,
+                            int32_t* partial_idx, void* workspace,
+                            size_t workspace_bytes, void* stream);
+
+/* Cross-part argmax (wiki summary, "Method": the final cross-rank argmax).
+ *   partial_val  fp32 [P][B], partial_idx int32 [P][B] (part-major)
+ *   P >= 1, B >= 0
+ * Per row: the largest value wins; on equal values the smaller id wins.
+ * Bit-exact: the result depends only on the set of pairs, not their order. */
+FS_API fs_status fs_merge(const float* partial_val, const int32_t* partial_idx, int32_t P,
+                   int32_t B, int32_t* out_ids, float* out_maxval, void* stream);
+
+/* The standard unfused decode step the method replaces (wiki summary,
+ * "Method", first paragraph): (1) matmul writing fp32 logits [B][V] to
+ * device memory, (2) softmax of z / T writing probabilities, (3)+(4)
+ * Gumbel perturbation of log-probabilities and argmax.  Same arguments,
+ * noise field and outputs as fs_sample (out_maxval is reported on the
+ * s = z / T + g scale by adding back each row's log-normaliser); workspace
+ * >= fs_unfused_workspace_bytes(B, D, V).  A baseline for measurement. */
+FS_API fs_status fs_sample_unfused(const void* h, const void* W, int32_t B, int32_t D,
+                            int32_t V, int32_t vocab_offset, const float* temperature,
+                            uint64_t seed, uint64_t step, int32_t* out_ids,
+                            float* out_maxval, void* workspace, size_t workspace_bytes,
+                            void* stream);
+
+/* Diagnostics: the device noise field, from the same device functions the
+ * samplers use.  Writes, for gv = gv0 .. gv0 + n - 1 of one (seed, step,
+ * row), the raw Philox word (out_bits, may be NULL) and the Gumbel value g
+ * (out_gumbel, may be NULL).  n >= 0; gv0 + n <= 2^32. */
+FS_API fs_status fs_debug_noise(uint64_t seed, uint64_t step, uint32_t row, uint32_t gv0,
+                         int64_t n, uint32_t* out_bits, float* out_gumbel,
+                         void* stream);
+
+/* Diagnostics: g = -log(-log u(x)) for n given words (device arrays). */
+FS_API fs_status fs_debug_gumbel(const uint32_t* bits, int64_t n, float* out_gumbel,
+                          void* stream);
+
+/* Kernel configurations of the fused sampler.  fs_force_config(id) pins
+ * every later fs_sample call in the process to configuration id (0 ..
+ * fs_num_configs() - 1); id = -1 restores the automatic choice.  Results do
+ * not depend on the configuration.  Not synchronised with concurrent calls. */
+FS_API int32_t fs_num_configs(void);
+FS_API const char* fs_config_name(int32_t id);
+FS_API fs_status fs_force_config(int32_t id);
+/* Configuration fs_sample would use for batch size B (after forcing). */
+FS_API int32_t fs_selected_config(int32_t B, int32_t D, int32_t V);
+
+/* Profiling of the fused kernel.  fs_profile_enable(capacity) creates
+ * 2 * capacity HIP events (outside any sampling call); while enabled, each of
+ * the next `capacity` fs_sample / fs_sample_partial calls records one event
+ * before and one after its fused-kernel launch, on the caller's stream.
+ * fs_profile_read waits for the recorded events, returns the number of timed
+ * launches and the sum, minimum and maximum of their durations in
+ * milliseconds (any output may be NULL), and re-arms the recorder.
+ * fs_profile_enable(0) destroys the events.  Not for concurrent callers. */
+FS_API fs_status fs_profile_enable(int32_t capacity);
+FS_API fs_status fs_profile_read(int32_t* launches, double* total_ms, double* min_ms,
+                                 double* max_ms);
+
+FS_API const char* fs_status_string(fs_status s);
+FS_API const char* fs_last_error(void);
+
+#ifdef __cplusplus
+}
+#endif
+
+#endif /* FLASHSAMPLE_H */

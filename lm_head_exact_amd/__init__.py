@@ -6,12 +6,15 @@ kernels, declared in ``include/flashsample.h``); the functions exported here
 only marshal torch tensors into that library.  The library is loaded on first
 use and a missing build raises instead of falling back to anything else.
 """
-__all__ = ["sample", "sample_partial", "merge", "sample_unfused", "workspace_bytes",
-           "unfused_workspace_bytes", "library_path"]
+_BINDING_NAMES = ("sample", "sample_partial", "merge", "sample_unfused", "workspace_bytes",
+                  "unfused_workspace_bytes", "library_path", "debug_noise", "debug_gumbel",
+                  "num_configs", "config_name", "profile_enable", "profile_read", "force_config", "selected_config",
+                  "FlashSampleError")
+__all__ = list(_BINDING_NAMES)
 
 
 def __getattr__(name):
-    if name in __all__:
+    if name in _BINDING_NAMES:
         from . import binding
         return getattr(binding, name)
     raise AttributeError(name)

@@ -1,0 +1,245 @@
+"""ctypes binding of libflashsample (C ABI in include/flashsample.h).
+
+Argument marshalling only: tensors are checked for device, dtype, shape and
+contiguity, outputs and workspaces are allocated with torch, and the call
+goes to the library on torch's current HIP stream.  Every step of the
+sampler runs in the library's kernels.  If the library is missing or fails
+to load, every function raises; there is no fallback path.
+"""
+import ctypes
+import os
+import re
+from typing import Optional, Tuple
+
+import torch  # loaded first, so the library binds to the same HIP runtime
+
+_HERE = os.path.dirname(os.path.abspath(__file__))
+_LIB_PATH = os.path.join(_HERE, "libflashsample.so")
+_HEADER = os.path.join(os.path.dirname(_HERE), "include", "flashsample.h")
+
+FS_OK, FS_ERR_INVALID_ARG, FS_ERR_UNSUPPORTED, FS_ERR_WORKSPACE, FS_ERR_HIP = range(5)
+
+
+class FlashSampleError(RuntimeError):
+    def __init__(self, status: int, message: str):
+        super().__init__(f"{_status_name(status)}: {message}")
+        self.status = status
+
+
+_lib = None
+
+
+def library_path() -> str:
+    return _LIB_PATH
+
+
+def exported_names_from_header():
+    """Names of every function the public header declares."""
+    text = open(_HEADER).read()
+    return sorted(set(re.findall(r"FS_API\s+[\w\s\*]+?\b(fs_\w+)\s*\(", text)))
+
+
+def lib():
+    """The loaded library (raises if it has not been built)."""
+    global _lib
+    if _lib is not None:
+        return _lib
+    if not os.path.exists(_LIB_PATH):
+        raise FlashSampleError(FS_ERR_UNSUPPORTED,
+                               f"{_LIB_PATH} is missing: run lm_head_exact_amd/build.py")
+    L = ctypes.CDLL(_LIB_PATH)
+    vp, i32, u32, i64, u64, sz = (ctypes.c_void_p, ctypes.c_int32, ctypes.c_uint32,
+                                  ctypes.c_int64, ctypes.c_uint64, ctypes.c_size_t)
+    sample_args = [vp, vp, i32, i32, i32, i32, vp, u64, u64, vp, vp, vp, sz, vp]
+    for name, args, res in [
+        ("fs_workspace_bytes", [i32, i32, i32], sz),
+        ("fs_unfused_workspace_bytes", [i32, i32, i32], sz),
+        ("fs_sample", sample_args, ctypes.c_int),
+        ("fs_sample_partial", sample_args, ctypes.c_int),
+        ("fs_sample_unfused", sample_args, ctypes.c_int),
+        ("fs_merge", [vp, vp, i32, i32, vp, vp, vp], ctypes.c_int),
+        ("fs_debug_noise", [u64, u64, u32, u32, i64, vp, vp, vp], ctypes.c_int),
+        ("fs_debug_gumbel", [vp, i64, vp, vp], ctypes.c_int),
+        ("fs_num_configs", [], i32),
+        ("fs_config_name", [i32], ctypes.c_char_p),
+        ("fs_force_config", [i32], ctypes.c_int),
+        ("fs_selected_config", [i32, i32, i32], i32),
+        ("fs_profile_enable", [i32], ctypes.c_int),
+        ("fs_profile_read", [ctypes.POINTER(ctypes.c_int32)] + [ctypes.POINTER(ctypes.c_double)] * 3,
+         ctypes.c_int),
+        ("fs_status_string", [ctypes.c_int], ctypes.c_char_p),
+        ("fs_last_error", [], ctypes.c_char_p),
+    ]:
+        fn = getattr(L, name)
+        fn.argtypes = args
+        fn.restype = res
+    _lib = L
+    return L
+
+
+def _status_name(s: int) -> str:
+    try:
+        return lib().fs_status_string(s).decode()
+    except Exception:
+        return f"status {s}"
+
+
+def _check(status: int):
+    if status != FS_OK:
+        raise FlashSampleError(status, lib().fs_last_error().decode())
+
+
+def _stream(device) -> ctypes.c_void_p:
+    return ctypes.c_void_p(torch.cuda.current_stream(device).cuda_stream)
+
+
+def _ptr(t: Optional[torch.Tensor]):
+    return ctypes.c_void_p(t.data_ptr()) if t is not None else None
+
+
+def _req(t: torch.Tensor, name: str, dtype, ndim: int):
+    if not isinstance(t, torch.Tensor):
+        raise TypeError(f"{name} must be a torch.Tensor")
+    if t.device.type != "cuda":
+        raise ValueError(f"{name} must be a device tensor (got {t.device})")
+    if t.dtype != dtype:
+        raise TypeError(f"{name} must be {dtype} (got {t.dtype})")
+    if t.dim() != ndim:
+        raise ValueError(f"{name} must have {ndim} dims (got {tuple(t.shape)})")
+    if not t.is_contiguous():
+        raise ValueError(f"{name} must be contiguous")
+
+
+def workspace_bytes(B: int, D: int, V: int) -> int:
+    return int(lib().fs_workspace_bytes(B, D, V))
+
+
+def unfused_workspace_bytes(B: int, D: int, V: int) -> int:
+    return int(lib().fs_unfused_workspace_bytes(B, D, V))
+
+
+def alloc_workspace(nbytes: int, device) -> torch.Tensor:
+    # torch's caching allocator returns 256-byte (or better) aligned blocks
+    return torch.empty(max(nbytes, 256), dtype=torch.uint8, device=device)
+
+
+def _sample_common(fn_name, h, W, temperature, seed, step, vocab_offset, out_a, out_b,
+                   workspace, ws_fn):
+    _req(h, "h", torch.bfloat16, 2)
+    _req(W, "W", torch.bfloat16, 2)
+    _req(temperature, "temperature", torch.float32, 1)
+    B, D = h.shape
+    V, D2 = W.shape
+    if D2 != D:
+        raise ValueError(f"h is B x {D} but W is V x {D2}")
+    if temperature.shape[0] != B:
+        raise ValueError("temperature must have B entries")
+    if not (h.device == W.device == temperature.device == out_a.device == out_b.device):
+        raise ValueError("all tensors must be on one device")
+    if workspace is None:
+        workspace = alloc_workspace(ws_fn(B, D, V), h.device)
+    fn = getattr(lib(), fn_name)
+    _check(fn(_ptr(h), _ptr(W), B, D, V, int(vocab_offset), _ptr(temperature),
+              int(seed) & (2**64 - 1), int(step) & (2**64 - 1), _ptr(out_a), _ptr(out_b),
+              _ptr(workspace), workspace.numel() * workspace.element_size(),
+              _stream(h.device)))
+
+
+def sample(h: torch.Tensor, W: torch.Tensor, temperature: torch.Tensor, seed: int, step: int,
+           vocab_offset: int = 0, out: Optional[Tuple[torch.Tensor, torch.Tensor]] = None,
+           workspace: Optional[torch.Tensor] = None):
+    """Fused LM-head + Gumbel-Max sampling: returns (ids int32[B], maxval fp32[B])."""
+    B = h.shape[0]
+    if out is None:
+        out = (torch.empty(B, dtype=torch.int32, device=h.device),
+               torch.empty(B, dtype=torch.float32, device=h.device))
+    ids, val = out
+    _sample_common("fs_sample", h, W, temperature, seed, step, vocab_offset, ids, val,
+                   workspace, workspace_bytes)
+    return ids, val
+
+
+def sample_partial(h, W, temperature, seed, step, vocab_offset, partial_val, partial_idx,
+                   workspace=None):
+    """One shard's per-row (max, global argmax) into partial_val / partial_idx (B each)."""
+    _req(partial_val, "partial_val", torch.float32, 1)
+    _req(partial_idx, "partial_idx", torch.int32, 1)
+    _sample_common("fs_sample_partial", h, W, temperature, seed, step, vocab_offset,
+                   partial_val, partial_idx, workspace, workspace_bytes)
+    return partial_val, partial_idx
+
+
+def sample_unfused(h, W, temperature, seed, step, vocab_offset=0, out=None, workspace=None):
+    """Unfused baseline (logits and probabilities in device memory)."""
+    B = h.shape[0]
+    if out is None:
+        out = (torch.empty(B, dtype=torch.int32, device=h.device),
+               torch.empty(B, dtype=torch.float32, device=h.device))
+    ids, val = out
+    _sample_common("fs_sample_unfused", h, W, temperature, seed, step, vocab_offset, ids, val,
+                   workspace, unfused_workspace_bytes)
+    return ids, val
+
+
+def merge(partial_val: torch.Tensor, partial_idx: torch.Tensor, out=None):
+    """Per-row argmax over P x B partials (largest value, then smallest id)."""
+    _req(partial_val, "partial_val", torch.float32, 2)
+    _req(partial_idx, "partial_idx", torch.int32, 2)
+    if partial_val.shape != partial_idx.shape:
+        raise ValueError("partial_val and partial_idx must have the same shape")
+    P, B = partial_val.shape
+    dev = partial_val.device
+    if out is None:
+        out = (torch.empty(B, dtype=torch.int32, device=dev),
+               torch.empty(B, dtype=torch.float32, device=dev))
+    ids, val = out
+    _check(lib().fs_merge(_ptr(partial_val), _ptr(partial_idx), P, B, _ptr(ids), _ptr(val),
+                          _stream(dev)))
+    return ids, val
+
+
+def debug_noise(seed: int, step: int, row: int, gv0: int, n: int, device="cuda"):
+    """Device noise words (as int32 bit patterns) and Gumbel values for ids gv0..gv0+n-1."""
+    bits = torch.empty(n, dtype=torch.int32, device=device)
+    g = torch.empty(n, dtype=torch.float32, device=device)
+    _check(lib().fs_debug_noise(int(seed), int(step), int(row), int(gv0), int(n), _ptr(bits),
+                                _ptr(g), _stream(bits.device)))
+    return bits, g
+
+
+def debug_gumbel(bits: torch.Tensor):
+    _req(bits, "bits", torch.int32, 1)
+    g = torch.empty(bits.shape[0], dtype=torch.float32, device=bits.device)
+    _check(lib().fs_debug_gumbel(_ptr(bits), bits.shape[0], _ptr(g), _stream(bits.device)))
+    return g
+
+
+def profile_enable(capacity: int):
+    """Time the next `capacity` fused-kernel launches with HIP events."""
+    _check(lib().fs_profile_enable(int(capacity)))
+
+
+def profile_read():
+    """(launches, total_ms, min_ms, max_ms) of the launches timed so far."""
+    n = ctypes.c_int32()
+    tot, lo, hi = ctypes.c_double(), ctypes.c_double(), ctypes.c_double()
+    _check(lib().fs_profile_read(ctypes.byref(n), ctypes.byref(tot), ctypes.byref(lo),
+                                 ctypes.byref(hi)))
+    return n.value, tot.value, lo.value, hi.value
+
+
+def num_configs() -> int:
+    return int(lib().fs_num_configs())
+
+
+def config_name(i: int) -> str:
+    r = lib().fs_config_name(i)
+    return r.decode() if r else ""
+
+
+def force_config(i: int):
+    _check(lib().fs_force_config(int(i)))
+
+
+def selected_config(B: int, D: int, V: int) -> int:
+    return int(lib().fs_selected_config(B, D, V))

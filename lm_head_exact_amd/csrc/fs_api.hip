@@ -1,0 +1,325 @@
+// fs_api.hip -- the C ABI of libflashsample (declared in include/flashsample.h).
+//
+// Every argument is checked here, on the host, before any HIP call; kernels
+// assume the checked invariants (D % 8 == 0 and 16-byte aligned operands for
+// the 16-byte fragment loads, ids that fit in int32, enough workspace).
+#include <atomic>
+#include <cstdarg>
+#include <cstdio>
+#include <cstdlib>
+#include <cstring>
+#include <mutex>
+#include <string>
+#include <vector>
+
+#include "../../include/flashsample.h"
+#include "fs_internal.hpp"
+
+namespace {
+
+thread_local std::string g_last_error;
+std::atomic<int> g_forced_config{-1};
+
+fs_status fail(fs_status s, const char* fmt, ...) __attribute__((format(printf, 2, 3)));
+
+fs_status fail(fs_status s, const char* fmt, ...) {
+  char buf[512];
+  va_list ap;
+  va_start(ap, fmt);
+  vsnprintf(buf, sizeof buf, fmt, ap);
+  va_end(ap);
+  g_last_error = buf;
+  return s;
+}
+
+fs_status hip_fail(hipError_t e, const char* what) {
+  return fail(FS_ERR_HIP, "%s: %s (%d)", what, hipGetErrorString(e), static_cast<int>(e));
+}
+
+bool aligned(const void* p, size_t a) { return (reinterpret_cast<uintptr_t>(p) % a) == 0; }
+
+constexpr int64_t kMaxId = 2147483647;  // ids are int32
+
+fs_status check_shape(int32_t B, int32_t D, int32_t V, int32_t vocab_offset) {
+  if (B < 0) return fail(FS_ERR_INVALID_ARG, "B must be >= 0 (got %d)", B);
+  if (D < 8 || D % 8 != 0)
+    return fail(FS_ERR_INVALID_ARG, "D must be a positive multiple of 8 (got %d)", D);
+  if (V < 1) return fail(FS_ERR_INVALID_ARG, "V must be >= 1 (got %d)", V);
+  if (vocab_offset < 0)
+    return fail(FS_ERR_INVALID_ARG, "vocab_offset must be >= 0 (got %d)", vocab_offset);
+  if (static_cast<int64_t>(vocab_offset) + V > kMaxId)
+    return fail(FS_ERR_INVALID_ARG, "vocab_offset + V exceeds 2^31 - 1 (%d + %d)", vocab_offset,
+                V);
+  return FS_OK;
+}
+
+fs_status check_sample_args(const void* h, const void* W, int32_t B, int32_t D, int32_t V,
+                            int32_t vocab_offset, const float* temperature, const void* out_a,
+                            const void* out_b, const void* workspace) {
+  fs_status s = check_shape(B, D, V, vocab_offset);
+  if (s != FS_OK || B == 0) return s;
+  if (!h || !W || !temperature || !out_a || !out_b || !workspace)
+    return fail(FS_ERR_INVALID_ARG, "null pointer argument");
+  if (!aligned(h, 16) || !aligned(W, 16))
+    return fail(FS_ERR_INVALID_ARG, "h and W must be 16-byte aligned");
+  if (!aligned(temperature, 4) || !aligned(out_a, 4) || !aligned(out_b, 4))
+    return fail(FS_ERR_INVALID_ARG, "temperature and outputs must be 4-byte aligned");
+  if (!aligned(workspace, 256)) return fail(FS_ERR_INVALID_ARG, "workspace must be 256-byte aligned");
+  return FS_OK;
+}
+
+size_t fused_workspace(int32_t B, int32_t V) {
+  const size_t S = (static_cast<size_t>(V) + fs::kMinRowsPerBlock - 1) / fs::kMinRowsPerBlock;
+  return fs::round_up(sizeof(float) * B * S, 256) + fs::round_up(sizeof(int32_t) * B * S, 256);
+}
+
+// Event pairs around fused-kernel launches (fs_profile_enable / _read).
+struct Profiler {
+  std::mutex mu;
+  std::atomic<bool> on{false};
+  std::vector<hipEvent_t> events;  // start, stop, start, stop, ...
+  int used = 0;
+};
+Profiler g_prof;
+
+void destroy_events() {
+  for (hipEvent_t e : g_prof.events) (void)hipEventDestroy(e);
+  g_prof.events.clear();
+  g_prof.used = 0;
+}
+
+int choose_config(int32_t B, int32_t D, int32_t V) {
+  const int forced = g_forced_config.load(std::memory_order_relaxed);
+  return forced >= 0 ? forced : fs::fused_auto_config(B, D, V);
+}
+
+// Shared body of fs_sample / fs_sample_partial.
+fs_status run_fused(const void* h, const void* W, int32_t B, int32_t D, int32_t V,
+                    int32_t vocab_offset, const float* temperature, uint64_t seed,
+                    uint64_t step, int32_t* out_ids, float* out_val, void* workspace,
+                    size_t workspace_bytes, void* stream, const char* who) {
+  fs_status s = check_sample_args(h, W, B, D, V, vocab_offset, temperature, out_ids, out_val,
+                                  workspace);
+  if (s != FS_OK || B == 0) return s;
+  const size_t need = fused_workspace(B, V);
+  if (workspace_bytes < need)
+    return fail(FS_ERR_WORKSPACE, "%s: workspace of %zu bytes is below the %zu required", who,
+                workspace_bytes, need);
+  const int cfg = choose_config(B, D, V);
+  const size_t S = (static_cast<size_t>(V) + fs::kMinRowsPerBlock - 1) / fs::kMinRowsPerBlock;
+  fs::SampleArgs a;
+  a.h = static_cast<const __bf16*>(h);
+  a.W = static_cast<const __bf16*>(W);
+  a.B = B;
+  a.D = D;
+  a.V = V;
+  a.vocab_offset = vocab_offset;
+  a.temperature = temperature;
+  a.seed = seed;
+  a.step = step;
+  a.part_val = static_cast<float*>(workspace);
+  a.part_idx = reinterpret_cast<int32_t*>(static_cast<char*>(workspace) +
+                                          fs::round_up(sizeof(float) * B * S, 256));
+  a.S = 0;
+  const hipStream_t st = static_cast<hipStream_t>(stream);
+  hipError_t e;
+  if (g_prof.on.load(std::memory_order_acquire)) {
+    std::lock_guard<std::mutex> lock(g_prof.mu);
+    const size_t k = 2 * static_cast<size_t>(g_prof.used);
+    const bool rec = k + 1 < g_prof.events.size();
+    if (rec && (e = hipEventRecord(g_prof.events[k], st)) != hipSuccess)
+      return hip_fail(e, "profile event");
+    e = fs::launch_fused(cfg, a, st);
+    if (e != hipSuccess) return hip_fail(e, "fused sampler launch");
+    if (rec) {
+      if ((e = hipEventRecord(g_prof.events[k + 1], st)) != hipSuccess)
+        return hip_fail(e, "profile event");
+      ++g_prof.used;
+    }
+  } else {
+    e = fs::launch_fused(cfg, a, st);
+    if (e != hipSuccess) return hip_fail(e, "fused sampler launch");
+  }
+  e = fs::launch_merge(a.part_val, a.part_idx, a.S, B, 1, a.S, out_ids, out_val, st);
+  if (e != hipSuccess) return hip_fail(e, "merge launch");
+  if (getenv("FS_LOG"))
+    fprintf(stderr, "[flashsample] %s B=%d D=%d V=%d config=%s splits=%d\n", who, B, D, V,
+            fs::fused_config_name(cfg), a.S);
+  return FS_OK;
+}
+
+}  // namespace
+
+extern "C" {
+
+size_t fs_workspace_bytes(int32_t B, int32_t D, int32_t V) {
+  if (check_shape(B, D, V, 0) != FS_OK) return 0;
+  return fused_workspace(B, V);
+}
+
+size_t fs_unfused_workspace_bytes(int32_t B, int32_t D, int32_t V) {
+  if (check_shape(B, D, V, 0) != FS_OK) return 0;
+  return fs::unfused_workspace_bytes(B, V);
+}
+
+fs_status fs_sample(const void* h, const void* W, int32_t B, int32_t D, int32_t V,
+                    int32_t vocab_offset, const float* temperature, uint64_t seed,
+                    uint64_t step, int32_t* out_ids, float* out_maxval, void* workspace,
+                    size_t workspace_bytes, void* stream) {
+  return run_fused(h, W, B, D, V, vocab_offset, temperature, seed, step, out_ids, out_maxval,
+                   workspace, workspace_bytes, stream, "fs_sample");
+}
+
+fs_status fs_sample_partial(const void* h, const void* W, int32_t B, int32_t D, int32_t V,
+                            int32_t vocab_offset, const float* temperature, uint64_t seed,
+                            uint64_t step, float* partial_val, int32_t* partial_idx,
+                            void* workspace, size_t workspace_bytes, void* stream) {
+  return run_fused(h, W, B, D, V, vocab_offset, temperature, seed, step, partial_idx,
+                   partial_val, workspace, workspace_bytes, stream, "fs_sample_partial");
+}
+
+fs_status fs_merge(const float* partial_val, const int32_t* partial_idx, int32_t P, int32_t B,
+                   int32_t* out_ids, float* out_maxval, void* stream) {
+  if (P < 1) return fail(FS_ERR_INVALID_ARG, "P must be >= 1 (got %d)", P);
+  if (B < 0) return fail(FS_ERR_INVALID_ARG, "B must be >= 0 (got %d)", B);
+  if (B == 0) return FS_OK;
+  if (!partial_val || !partial_idx || !out_ids || !out_maxval)
+    return fail(FS_ERR_INVALID_ARG, "null pointer argument");
+  if (!aligned(partial_val, 4) || !aligned(partial_idx, 4) || !aligned(out_ids, 4) ||
+      !aligned(out_maxval, 4))
+    return fail(FS_ERR_INVALID_ARG, "pointers must be 4-byte aligned");
+  if (static_cast<int64_t>(P) * B > (int64_t{1} << 40))
+    return fail(FS_ERR_INVALID_ARG, "P * B too large");
+  hipError_t e = fs::launch_merge(partial_val, partial_idx, P, B, B, 1, out_ids, out_maxval,
+                                  static_cast<hipStream_t>(stream));
+  if (e != hipSuccess) return hip_fail(e, "merge launch");
+  return FS_OK;
+}
+
+fs_status fs_sample_unfused(const void* h, const void* W, int32_t B, int32_t D, int32_t V,
+                            int32_t vocab_offset, const float* temperature, uint64_t seed,
+                            uint64_t step, int32_t* out_ids, float* out_maxval,
+                            void* workspace, size_t workspace_bytes, void* stream) {
+  fs_status s = check_sample_args(h, W, B, D, V, vocab_offset, temperature, out_ids,
+                                  out_maxval, workspace);
+  if (s != FS_OK || B == 0) return s;
+  const size_t need = fs::unfused_workspace_bytes(B, V);
+  if (workspace_bytes < need)
+    return fail(FS_ERR_WORKSPACE, "fs_sample_unfused: workspace of %zu bytes is below the %zu required",
+                workspace_bytes, need);
+  fs::SampleArgs a;
+  a.h = static_cast<const __bf16*>(h);
+  a.W = static_cast<const __bf16*>(W);
+  a.B = B;
+  a.D = D;
+  a.V = V;
+  a.vocab_offset = vocab_offset;
+  a.temperature = temperature;
+  a.seed = seed;
+  a.step = step;
+  a.part_val = nullptr;
+  a.part_idx = nullptr;
+  a.S = 0;
+  hipError_t e = fs::launch_unfused(a, out_ids, out_maxval, workspace,
+                                    static_cast<hipStream_t>(stream));
+  if (e != hipSuccess) return hip_fail(e, "unfused sampler launch");
+  return FS_OK;
+}
+
+fs_status fs_debug_noise(uint64_t seed, uint64_t step, uint32_t row, uint32_t gv0, int64_t n,
+                         uint32_t* out_bits, float* out_gumbel, void* stream) {
+  if (n < 0) return fail(FS_ERR_INVALID_ARG, "n must be >= 0");
+  if (static_cast<uint64_t>(gv0) + static_cast<uint64_t>(n) > (uint64_t{1} << 32))
+    return fail(FS_ERR_INVALID_ARG, "gv0 + n exceeds 2^32");
+  if (n == 0 || (!out_bits && !out_gumbel)) return FS_OK;
+  if ((out_bits && !aligned(out_bits, 4)) || (out_gumbel && !aligned(out_gumbel, 4)))
+    return fail(FS_ERR_INVALID_ARG, "outputs must be 4-byte aligned");
+  hipError_t e = fs::launch_debug_noise(seed, step, row, gv0, n, out_bits, out_gumbel,
+                                        static_cast<hipStream_t>(stream));
+  if (e != hipSuccess) return hip_fail(e, "noise launch");
+  return FS_OK;
+}
+
+fs_status fs_debug_gumbel(const uint32_t* bits, int64_t n, float* out_gumbel, void* stream) {
+  if (n < 0) return fail(FS_ERR_INVALID_ARG, "n must be >= 0");
+  if (n == 0) return FS_OK;
+  if (!bits || !out_gumbel) return fail(FS_ERR_INVALID_ARG, "null pointer argument");
+  if (!aligned(bits, 4) || !aligned(out_gumbel, 4))
+    return fail(FS_ERR_INVALID_ARG, "pointers must be 4-byte aligned");
+  hipError_t e = fs::launch_debug_gumbel(bits, n, out_gumbel, static_cast<hipStream_t>(stream));
+  if (e != hipSuccess) return hip_fail(e, "gumbel launch");
+  return FS_OK;
+}
+
+fs_status fs_profile_enable(int32_t capacity) {
+  if (capacity < 0) return fail(FS_ERR_INVALID_ARG, "capacity must be >= 0");
+  std::lock_guard<std::mutex> lock(g_prof.mu);
+  g_prof.on.store(false, std::memory_order_release);
+  destroy_events();
+  if (capacity == 0) return FS_OK;
+  g_prof.events.resize(2 * static_cast<size_t>(capacity));
+  for (auto& ev : g_prof.events) {
+    hipError_t e = hipEventCreate(&ev);
+    if (e != hipSuccess) {
+      ev = nullptr;
+      destroy_events();
+      return hip_fail(e, "hipEventCreate");
+    }
+  }
+  g_prof.on.store(true, std::memory_order_release);
+  return FS_OK;
+}
+
+fs_status fs_profile_read(int32_t* launches, double* total_ms, double* min_ms,
+                          double* max_ms) {
+  std::lock_guard<std::mutex> lock(g_prof.mu);
+  double tot = 0.0, lo = 0.0, hi = 0.0;
+  for (int i = 0; i < g_prof.used; ++i) {
+    hipError_t e = hipEventSynchronize(g_prof.events[2 * i + 1]);
+    if (e != hipSuccess) return hip_fail(e, "hipEventSynchronize");
+    float ms = 0.f;
+    e = hipEventElapsedTime(&ms, g_prof.events[2 * i], g_prof.events[2 * i + 1]);
+    if (e != hipSuccess) return hip_fail(e, "hipEventElapsedTime");
+    tot += ms;
+    lo = (i == 0 || ms < lo) ? ms : lo;
+    hi = (i == 0 || ms > hi) ? ms : hi;
+  }
+  if (launches) *launches = g_prof.used;
+  if (total_ms) *total_ms = tot;
+  if (min_ms) *min_ms = lo;
+  if (max_ms) *max_ms = hi;
+  g_prof.used = 0;
+  return FS_OK;
+}
+
+int32_t fs_num_configs(void) { return fs::num_fused_configs(); }
+
+const char* fs_config_name(int32_t id) { return fs::fused_config_name(id); }
+
+fs_status fs_force_config(int32_t id) {
+  if (id < -1 || id >= fs::num_fused_configs())
+    return fail(FS_ERR_INVALID_ARG, "config id %d out of range [-1, %d)", id,
+                fs::num_fused_configs());
+  g_forced_config.store(id, std::memory_order_relaxed);
+  return FS_OK;
+}
+
+int32_t fs_selected_config(int32_t B, int32_t D, int32_t V) {
+  if (check_shape(B, D, V, 0) != FS_OK) return -1;
+  return choose_config(B, D, V);
+}
+
+const char* fs_status_string(fs_status s) {
+  switch (s) {
+    case FS_OK: return "FS_OK";
+    case FS_ERR_INVALID_ARG: return "FS_ERR_INVALID_ARG";
+    case FS_ERR_UNSUPPORTED: return "FS_ERR_UNSUPPORTED";
+    case FS_ERR_WORKSPACE: return "FS_ERR_WORKSPACE";
+    case FS_ERR_HIP: return "FS_ERR_HIP";
+  }
+  return "FS_ERR_UNKNOWN";
+}
+
+const char* fs_last_error(void) { return g_last_error.c_str(); }
+
+}  // extern "C"

@@ -1,0 +1,116 @@
+// fs_device.hpp -- device building blocks of libflashsample (gfx950).
+//
+// Counter-based noise, the uniform -> Gumbel map, the (max, argmax)
+// comparator and wave-level reductions shared by the fused sampler, the
+// unfused baseline and the diagnostics.  Written for CDNA4: 64-lane
+// wavefronts, bf16 MFMA operand vectors.
+#pragma once
+
+#include <hip/hip_runtime.h>
+#include <stdint.h>
+
+namespace fs {
+
+typedef __bf16 bf16x8 __attribute__((ext_vector_type(8)));
+typedef float f32x4 __attribute__((ext_vector_type(4)));
+typedef float f32x16 __attribute__((ext_vector_type(16)));
+typedef uint32_t u32x4 __attribute__((ext_vector_type(4)));
+
+constexpr int kWave = 64;
+
+// ---------------------------------------------------------------------------
+// Philox-4x32-10 (Salmon, Moraes, Dror, Shaw, SC'11).  Each round multiplies
+// counter words 0 and 2 by two fixed odd 32-bit constants; the high halves,
+// xored with the other two words and the round key, and the low halves form
+// the next counter.  The key advances by two Weyl increments per round.  The
+// key words are uniform across the wave, so the compiler keeps the schedule
+// in scalar registers.
+// ---------------------------------------------------------------------------
+struct Philox {
+  uint32_t k0, k1;
+
+  __device__ __forceinline__ explicit Philox(uint64_t seed)
+      : k0(static_cast<uint32_t>(seed)), k1(static_cast<uint32_t>(seed >> 32)) {}
+
+  __device__ __forceinline__ u32x4 operator()(u32x4 c) const {
+    uint32_t a = k0, b = k1;
+#pragma unroll
+    for (int r = 0; r < 10; ++r) {
+      const uint64_t p = static_cast<uint64_t>(0xD2511F53u) * c.x;
+      const uint64_t q = static_cast<uint64_t>(0xCD9E8D57u) * c.z;
+      const uint32_t p_hi = static_cast<uint32_t>(p >> 32), p_lo = static_cast<uint32_t>(p);
+      const uint32_t q_hi = static_cast<uint32_t>(q >> 32), q_lo = static_cast<uint32_t>(q);
+      c = u32x4{q_hi ^ c.y ^ a, q_lo, p_hi ^ c.w ^ b, p_lo};
+      a += 0x9E3779B9u;
+      b += 0xBB67AE85u;
+    }
+    return c;
+  }
+};
+
+// Counter of the block that holds global id gv for batch row `row`: one
+// block serves the four ids 4m .. 4m+3 (word gv mod 4).
+__device__ __forceinline__ u32x4 noise_counter(uint32_t gv, uint32_t row, uint64_t step) {
+  return u32x4{gv >> 2, row, static_cast<uint32_t>(step), static_cast<uint32_t>(step >> 32)};
+}
+
+__device__ __forceinline__ uint32_t pick_word(u32x4 w, uint32_t i) {
+  return i == 0 ? w.x : i == 1 ? w.y : i == 2 ? w.z : w.w;
+}
+
+// Standard Gumbel value of a 32-bit word: u = (2k+1) 2^-24 with k the top 23
+// bits, g = -log(-log u).  The winners of a large vocabulary sit at u close
+// to 1 where -log u ~ 1 - u is tiny, so -log u is evaluated as
+// -log1p(-(1 - u)) from the complement 1 - u = (2^24 - 1 - 2k) 2^-24, which
+// is exact in fp32: the relative error of -log u stays at the library's few
+// ulp over the whole grid instead of growing as u -> 1.
+__device__ __forceinline__ float gumbel_from_bits(uint32_t x) {
+  const uint32_t k = x >> 9;
+  const float one_minus_u = static_cast<float>(0xFFFFFFu - 2u * k) * 0x1p-24f;
+  const float e = -log1pf(-one_minus_u);  // -log u > 0
+  return -logf(e);
+}
+
+// ---------------------------------------------------------------------------
+// (value, id) maximum with ties to the smaller id.
+// ---------------------------------------------------------------------------
+__device__ __forceinline__ bool better(float v, int32_t i, float bv, int32_t bi) {
+  return v > bv || (v == bv && i < bi);
+}
+
+struct ArgMax {
+  float v;
+  int32_t i;
+  __device__ __forceinline__ void init() {
+    v = -__builtin_inff();
+    i = 0x7FFFFFFF;
+  }
+  __device__ __forceinline__ void push(float nv, int32_t ni) {
+    if (better(nv, ni, v, i)) {
+      v = nv;
+      i = ni;
+    }
+  }
+  // Combine with the pair held by lane (lane ^ mask).
+  __device__ __forceinline__ void xor_reduce(int mask) {
+    const float ov = __shfl_xor(v, mask, kWave);
+    const int32_t oi = __shfl_xor(i, mask, kWave);
+    push(ov, oi);
+  }
+};
+
+// Row temperature -> (greedy flag, fp32 reciprocal).  Greedy when T is not a
+// positive number (0, -0, negative, NaN): the T -> 0 limit of the sampler.
+__device__ __forceinline__ bool row_is_greedy(float T) { return !(T > 0.0f); }
+
+__device__ __forceinline__ float row_inv_temperature(float T) {
+  return row_is_greedy(T) ? 1.0f : __fdiv_rn(1.0f, T);
+}
+
+// Perturbed score of one logit: fp32 multiply then fp32 add, kept as two
+// separately rounded operations (no contraction into a fused multiply-add).
+__device__ __forceinline__ float perturbed_score(float z, float inv_t, float g) {
+  return __fadd_rn(__fmul_rn(z, inv_t), g);
+}
+
+}  // namespace fs

@@ -1,0 +1,49 @@
+// fs_internal.hpp -- host-side interface between the C ABI (fs_api.hip) and
+// the kernel translation units.  Not installed; not part of the ABI.
+#pragma once
+
+#include <hip/hip_runtime.h>
+#include <stddef.h>
+#include <stdint.h>
+
+namespace fs {
+
+struct SampleArgs {
+  const __bf16* h;
+  const __bf16* W;
+  int32_t B, D, V, vocab_offset;
+  const float* temperature;
+  uint64_t seed, step;
+  float* part_val;    // [B][S] per-block partial maxima
+  int32_t* part_idx;  // [B][S] their global ids
+  int32_t S;          // number of vocabulary blocks (set by the launcher)
+};
+
+// ---- fused sampler (fs_fused.hip) ----
+int num_fused_configs();
+const char* fused_config_name(int id);
+int fused_rows_per_block(int id);
+int fused_auto_config(int32_t B, int32_t D, int32_t V);
+// Smallest rows-per-block over all configurations: bounds the split count.
+constexpr int kMinRowsPerBlock = 64;
+// Launch configuration `id`; sets a.S to the number of vocabulary blocks.
+hipError_t launch_fused(int id, SampleArgs& a, hipStream_t stream);
+
+// Per-row argmax over P partials; element (p, b) at p * stride_p + b * stride_b.
+hipError_t launch_merge(const float* val, const int32_t* idx, int32_t P, int32_t B,
+                        int64_t stride_p, int64_t stride_b, int32_t* out_ids,
+                        float* out_val, hipStream_t stream);
+
+hipError_t launch_debug_noise(uint64_t seed, uint64_t step, uint32_t row, uint32_t gv0,
+                              int64_t n, uint32_t* bits, float* g, hipStream_t stream);
+hipError_t launch_debug_gumbel(const uint32_t* bits, int64_t n, float* g,
+                               hipStream_t stream);
+
+// ---- unfused baseline (fs_unfused.hip) ----
+size_t unfused_workspace_bytes(int32_t B, int32_t V);
+hipError_t launch_unfused(const SampleArgs& a, int32_t* out_ids, float* out_val,
+                          void* workspace, hipStream_t stream);
+
+inline size_t round_up(size_t x, size_t a) { return (x + a - 1) / a * a; }
+
+}  // namespace fs

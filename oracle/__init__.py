@@ -74,8 +74,15 @@ def _load():
             fn = getattr(lib, name)
             fn.argtypes = [ctypes.c_void_p, ctypes.c_int64, ctypes.c_void_p]
             fn.restype = None
+        lib.oracle_max_threads.argtypes = []
+        lib.oracle_max_threads.restype = ctypes.c_int
         _lib = lib
     return _lib
+
+
+def max_threads() -> int:
+    """OpenMP threads the oracle's parallel loops use."""
+    return int(_load().oracle_max_threads())
 
 
 def _ptr(a):

@@ -36,11 +36,15 @@
  * output depends on the thread count or the schedule.
  */
 #include <math.h>
+#include <omp.h>
 #include <stddef.h>
 #include <stdint.h>
 #include <string.h>
 
 #define ORACLE_EXPORT __attribute__((visibility("default")))
+
+/* Threads an OpenMP region of the oracle will use. */
+ORACLE_EXPORT int oracle_max_threads(void) { return omp_get_max_threads(); }
 
 /* ---------------------------------------------------------------------- */
 /* Philox-4x32-10 (SC'11 paper, section 5: the Philox round is two 32x32->64

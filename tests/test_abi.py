@@ -1,0 +1,106 @@
+"""The C-ABI library loads, exports what include/flashsample.h declares, and
+rejects bad arguments on the host before any HIP call (CPU only: no call in
+this file reaches a kernel launch)."""
+import ctypes
+
+import pytest
+
+from lm_head_exact_amd import binding as bd
+
+ALIGNED = 0x10000            # fake, never dereferenced: every call below fails validation
+WS_ALIGNED = 0x20000
+
+
+@pytest.fixture(scope="module")
+def L():
+    return bd.lib()
+
+
+def test_exports_every_declared_symbol(L):
+    names = bd.exported_names_from_header()
+    assert len(names) >= 14
+    for n in names:
+        assert hasattr(L, n), f"{n} declared in flashsample.h but not exported"
+
+
+def test_status_strings(L):
+    assert L.fs_status_string(0) == b"FS_OK"
+    assert L.fs_status_string(4) == b"FS_ERR_HIP"
+    assert L.fs_status_string(99) == b"FS_ERR_UNKNOWN"
+
+
+def _sample(L, fn="fs_sample", h=ALIGNED, W=ALIGNED, B=4, D=256, V=1000, off=0,
+            T=ALIGNED, ids=ALIGNED, val=ALIGNED, ws=WS_ALIGNED, wsb=1 << 30):
+    return getattr(L, fn)(h, W, B, D, V, off, T, 1, 2, ids, val, ws, wsb, None)
+
+
+@pytest.mark.parametrize("fn", ["fs_sample", "fs_sample_partial", "fs_sample_unfused"])
+@pytest.mark.parametrize("kw,status", [
+    (dict(D=7), bd.FS_ERR_INVALID_ARG),
+    (dict(D=0), bd.FS_ERR_INVALID_ARG),
+    (dict(D=260), bd.FS_ERR_INVALID_ARG),
+    (dict(V=0), bd.FS_ERR_INVALID_ARG),
+    (dict(B=-1), bd.FS_ERR_INVALID_ARG),
+    (dict(off=-5), bd.FS_ERR_INVALID_ARG),
+    (dict(off=2**31 - 1000, V=1000), bd.FS_ERR_INVALID_ARG),
+    (dict(h=None), bd.FS_ERR_INVALID_ARG),
+    (dict(W=None), bd.FS_ERR_INVALID_ARG),
+    (dict(T=None), bd.FS_ERR_INVALID_ARG),
+    (dict(ids=None), bd.FS_ERR_INVALID_ARG),
+    (dict(ws=None), bd.FS_ERR_INVALID_ARG),
+    (dict(h=ALIGNED + 8), bd.FS_ERR_INVALID_ARG),
+    (dict(W=ALIGNED + 2), bd.FS_ERR_INVALID_ARG),
+    (dict(T=ALIGNED + 1), bd.FS_ERR_INVALID_ARG),
+    (dict(ws=WS_ALIGNED + 16), bd.FS_ERR_INVALID_ARG),
+    (dict(wsb=16), bd.FS_ERR_WORKSPACE),
+    (dict(B=0, h=None, W=None, T=None, ids=None, val=None, ws=None), bd.FS_OK),
+])
+def test_argument_errors(L, fn, kw, status):
+    assert _sample(L, fn, **kw) == status
+    if status != bd.FS_OK:
+        assert len(L.fs_last_error()) > 0
+
+
+def test_workspace_sizes(L):
+    assert L.fs_workspace_bytes(0, 256, 1000) == 0 or L.fs_workspace_bytes(0, 256, 1000) >= 0
+    assert L.fs_workspace_bytes(4, 7, 1000) == 0          # invalid D
+    ws = L.fs_workspace_bytes(32, 4096, 128256)
+    assert ws >= 8 * 32 * (128256 // 64) and ws % 256 == 0
+    unf = L.fs_unfused_workspace_bytes(32, 4096, 128256)
+    assert unf >= 2 * 4 * 32 * 128256                     # logits + probabilities
+    # exactly-sized workspace passes the size check (then fails on alignment)
+    need = L.fs_workspace_bytes(4, 256, 1000)
+    assert _sample(L, wsb=need - 1) == bd.FS_ERR_WORKSPACE
+    assert _sample(L, wsb=need, ws=WS_ALIGNED + 4) == bd.FS_ERR_INVALID_ARG
+
+
+def test_merge_argument_errors(L):
+    assert L.fs_merge(ALIGNED, ALIGNED, 0, 4, ALIGNED, ALIGNED, None) == bd.FS_ERR_INVALID_ARG
+    assert L.fs_merge(ALIGNED, ALIGNED, 2, -1, ALIGNED, ALIGNED, None) == bd.FS_ERR_INVALID_ARG
+    assert L.fs_merge(None, ALIGNED, 2, 4, ALIGNED, ALIGNED, None) == bd.FS_ERR_INVALID_ARG
+    assert L.fs_merge(ALIGNED + 2, ALIGNED, 2, 4, ALIGNED, ALIGNED, None) == bd.FS_ERR_INVALID_ARG
+    assert L.fs_merge(None, None, 3, 0, None, None, None) == bd.FS_OK
+
+
+def test_debug_argument_errors(L):
+    assert L.fs_debug_noise(0, 0, 0, 0, -1, ALIGNED, ALIGNED, None) == bd.FS_ERR_INVALID_ARG
+    assert L.fs_debug_noise(0, 0, 0, 2**32 - 4, 5, ALIGNED, ALIGNED, None) == bd.FS_ERR_INVALID_ARG
+    assert L.fs_debug_noise(0, 0, 0, 0, 0, None, None, None) == bd.FS_OK
+    assert L.fs_debug_gumbel(None, 5, ALIGNED, None) == bd.FS_ERR_INVALID_ARG
+
+
+def test_configs(L):
+    n = L.fs_num_configs()
+    assert n >= 5
+    names = [L.fs_config_name(i).decode() for i in range(n)]
+    assert len(set(names)) == n
+    assert L.fs_config_name(n) is None
+    assert L.fs_force_config(n) == bd.FS_ERR_INVALID_ARG
+    assert L.fs_force_config(-2) == bd.FS_ERR_INVALID_ARG
+    auto = [L.fs_selected_config(B, 4096, 128256) for B in (1, 32, 64, 128, 256)]
+    assert all(0 <= c < n for c in auto)
+    assert L.fs_force_config(n - 1) == bd.FS_OK
+    assert L.fs_selected_config(1, 4096, 128256) == n - 1
+    assert L.fs_force_config(-1) == bd.FS_OK
+    assert L.fs_selected_config(1, 4096, 128256) == auto[0]
+    assert L.fs_selected_config(1, 7, 10) == -1
