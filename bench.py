@@ -116,10 +116,10 @@ def main():
         out = (torch.empty(B, dtype=torch.int32, device=dev),
                torch.empty(B, dtype=torch.float32, device=dev))
         if unfused:
-            ws = fsl.binding.alloc_workspace(fsl.unfused_workspace_bytes(B, D, V), dev)
+            ws = fsl.alloc_workspace(fsl.unfused_workspace_bytes(B, D, V), dev)
             call = fsl.sample_unfused
         else:
-            ws = fsl.binding.alloc_workspace(fsl.workspace_bytes(B, D, V), dev)
+            ws = fsl.alloc_workspace(fsl.workspace_bytes(B, D, V), dev)
             call = fsl.sample
 
         def fn(i):

@@ -9,11 +9,14 @@ use and a missing build raises instead of falling back to anything else.
 _BINDING_NAMES = ("sample", "sample_partial", "merge", "sample_unfused", "workspace_bytes",
                   "unfused_workspace_bytes", "library_path", "debug_noise", "debug_gumbel",
                   "num_configs", "config_name", "profile_enable", "profile_read", "force_config", "selected_config",
-                  "FlashSampleError")
+                  "FlashSampleError", "alloc_workspace")
 __all__ = list(_BINDING_NAMES)
 
 
 def __getattr__(name):
+    if name == "binding":
+        import importlib
+        return importlib.import_module(".binding", __name__)
     if name in _BINDING_NAMES:
         from . import binding
         return getattr(binding, name)

@@ -9,6 +9,9 @@
 #include <hip/hip_runtime.h>
 #include <stdint.h>
 
+#include <type_traits>
+#include <utility>
+
 namespace fs {
 
 typedef __bf16 bf16x8 __attribute__((ext_vector_type(8)));
@@ -17,6 +20,21 @@ typedef float f32x16 __attribute__((ext_vector_type(16)));
 typedef uint32_t u32x4 __attribute__((ext_vector_type(4)));
 
 constexpr int kWave = 64;
+
+// Compile-time loop: f(std::integral_constant<int, 0>) ... f(<N-1>).  Register
+// arrays (accumulators, per-row maxima) are only indexed with these constants,
+// so they never fall back to scratch memory whatever the unroller decides.
+// Loop bodies are lambdas marked FS_INLINE: a body left as a call would force
+// the arrays it captures into addressable (scratch) memory.
+#define FS_INLINE __attribute__((always_inline))
+template <class F, int... I>
+__device__ __forceinline__ void static_for_impl(F&& f, std::integer_sequence<int, I...>) {
+  (f(std::integral_constant<int, I>{}), ...);
+}
+template <int N, class F>
+__device__ __forceinline__ void static_for(F&& f) {
+  static_for_impl(f, std::make_integer_sequence<int, N>{});
+}
 
 // ---------------------------------------------------------------------------
 // Philox-4x32-10 (Salmon, Moraes, Dror, Shaw, SC'11).  Each round multiplies

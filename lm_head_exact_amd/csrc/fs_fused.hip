@@ -7,73 +7,88 @@
 // decomposes over any partition of the vocabulary ("Key claims"), the result
 // equals one global argmax over the full noise field.
 //
-// Grid: x = vocabulary blocks of NW * MR * 16 rows, y = batch blocks of
-// NT * 16 rows.  Each wave owns MR * 16 consecutive vocabulary rows and all
-// NT * 16 batch rows of its block, so every W element is read by one wave
-// exactly once.  The epilogue runs in registers on the MFMA accumulators;
-// the block writes one partial per batch row to part_[val|idx][b][block].
+// Grid: x = vocabulary blocks of Loop::kRowsPerBlock rows, y = batch blocks of
+// NT * 16 rows.  The main loop (fs_mma.hpp) is a policy that leaves each
+// wave with MFMA accumulators for MR * 16 vocabulary rows x NT * 16 batch
+// rows; the epilogue runs in registers on those accumulators and the block
+// writes one (max, argmax) partial per batch row to part_[val|idx][b][block].
 #include "fs_internal.hpp"
 #include "fs_mma.hpp"
 
 namespace fs {
 
-template <int MR, int NT, int NW, bool ALIGN4>
-__global__ __launch_bounds__(NW * kWave) void fused_sample_kernel(SampleArgs a) {
+template <class Loop, bool ALIGN4>
+__global__ __launch_bounds__(Loop::NW * kWave)
+__attribute__((amdgpu_waves_per_eu(Loop::kWavesPerSimd))) void fused_sample_kernel(SampleArgs a) {
+  constexpr int MR = Loop::MR, NT = Loop::NT, NW = Loop::NW;
+  extern __shared__ __attribute__((aligned(16))) unsigned char dyn_smem[];
   const int lane = threadIdx.x & (kWave - 1);
   const int wave = threadIdx.x >> 6;
   const int li = lane & 15, kb = lane >> 4;
-  const int row0 = (blockIdx.x * NW + wave) * (MR * 16);
+  const int row0 = Loop::row0(blockIdx.x, wave);
   const int col0 = blockIdx.y * (NT * 16);
 
   f32x4 acc[MR][NT];
-  mma_block<MR, NT>(a.W, a.h, a.B, a.D, a.V, row0, col0, acc);
+  Loop::run(a.W, a.h, a.B, a.D, a.V, row0, col0, acc, dyn_smem);
 
   // ---- epilogue: scale, perturb, running (max, argmax) per batch row ----
+  // Lane (li, kb) holds batch row col0 + 16n + li and vocabulary rows
+  // row0 + 16m + 4kb + r, r = 0..3: one Philox block when vocab_offset % 4 == 0.
   const Philox philox(a.seed);
   ArgMax best[NT];
-#pragma unroll
-  for (int n = 0; n < NT; ++n) {
+  static_for<NT>([&](auto n) FS_INLINE {
     best[n].init();
     const int b = col0 + n * 16 + li;
-    if (b >= a.B) continue;
-    const float T = a.temperature[b];
-    const bool greedy = row_is_greedy(T);
-    const float inv_t = row_inv_temperature(T);
-#pragma unroll
-    for (int m = 0; m < MR; ++m) {
-      const int v0 = row0 + m * 16 + 4 * kb;  // a multiple of 4
-      const uint32_t gv0 = static_cast<uint32_t>(a.vocab_offset + v0);
-      u32x4 words = u32x4{0u, 0u, 0u, 0u};
-      if (ALIGN4 && !greedy) words = philox(noise_counter(gv0, b, a.step));
-#pragma unroll
-      for (int r = 0; r < 4; ++r) {
-        if (v0 + r >= a.V) break;
-        const uint32_t gv = gv0 + r;
-        float s = acc[m][n][r];
-        if (!greedy) {
-          const uint32_t x = ALIGN4 ? pick_word(words, r)
-                                    : pick_word(philox(noise_counter(gv, b, a.step)), gv & 3u);
-          s = perturbed_score(s, inv_t, gumbel_from_bits(x));
+    if (b < a.B) {
+      const float T = a.temperature[b];
+      const bool greedy = row_is_greedy(T);
+      const float inv_t = row_inv_temperature(T);
+      static_for<MR>([&](auto m) FS_INLINE {
+        if (Loop::owns(wave, m, n)) {
+          const int v0 = row0 + m * 16 + 4 * kb;  // a multiple of 4
+          const uint32_t gv0 = static_cast<uint32_t>(a.vocab_offset + v0);
+          // ids gv0 .. gv0+3 lie in Philox blocks gv0/4 and (when vocab_offset
+          // is not a multiple of 4) gv0/4 + 1
+          u32x4 w0 = u32x4{0u, 0u, 0u, 0u}, w1 = w0;
+          if (!greedy) {
+            w0 = philox(noise_counter(gv0, b, a.step));
+            if (!ALIGN4) w1 = philox(noise_counter(gv0 + 4u, b, a.step));
+          }
+          static_for<4>([&](auto rc) FS_INLINE {
+            constexpr int r = decltype(rc)::value;
+            if (v0 + r < a.V) {
+              const uint32_t gv = gv0 + r;
+              float s = acc[m][n][r];
+              if (!greedy) {
+                uint32_t x;
+                if (ALIGN4) {
+                  x = w0[r];
+                } else {
+                  const uint32_t q = (gv0 & 3u) + r;  // word index across the two blocks
+                  x = q < 4u ? pick_word(w0, q) : pick_word(w1, q - 4u);
+                }
+                s = perturbed_score(s, inv_t, gumbel_from_bits(x));
+              }
+              best[n].push(s, static_cast<int32_t>(gv));
+            }
+          });
         }
-        best[n].push(s, static_cast<int32_t>(gv));
-      }
+      });
     }
-  }
+  });
   // lanes l, l^16, l^32, l^48 hold the same batch row
-#pragma unroll
-  for (int n = 0; n < NT; ++n) {
+  static_for<NT>([&](auto n) FS_INLINE {
     best[n].xor_reduce(16);
     best[n].xor_reduce(32);
-  }
+  });
 
   __shared__ float s_val[NW][NT * 16];
   __shared__ int32_t s_idx[NW][NT * 16];
   if (kb == 0) {
-#pragma unroll
-    for (int n = 0; n < NT; ++n) {
+    static_for<NT>([&](auto n) FS_INLINE {
       s_val[wave][n * 16 + li] = best[n].v;
       s_idx[wave][n * 16 + li] = best[n].i;
-    }
+    });
   }
   __syncthreads();
   for (int c = threadIdx.x; c < NT * 16; c += NW * kWave) {
@@ -136,38 +151,86 @@ __global__ __launch_bounds__(256) void debug_gumbel_kernel(const uint32_t* bits,
 // ---------------------------------------------------------------------------
 namespace {
 
-template <int MR, int NT, int NW>
+template <class Loop>
 hipError_t launch_cfg(SampleArgs& a, hipStream_t stream) {
-  constexpr int rows = MR * 16 * NW;
+  constexpr int rows = Loop::kRowsPerBlock;
   static_assert(rows >= kMinRowsPerBlock, "split count bound");
+  if (!Loop::supports(a.D)) return hipErrorInvalidValue;
+  constexpr size_t smem = Loop::kSmemBytes;
+  if (smem > 0) {  // may exceed the default dynamic-LDS limit: raise it once per kernel
+    static const hipError_t attr = [] {
+      hipError_t e = hipFuncSetAttribute(
+          reinterpret_cast<const void*>(&fused_sample_kernel<Loop, true>),
+          hipFuncAttributeMaxDynamicSharedMemorySize, static_cast<int>(smem));
+      if (e != hipSuccess) return e;
+      return hipFuncSetAttribute(reinterpret_cast<const void*>(&fused_sample_kernel<Loop, false>),
+                                 hipFuncAttributeMaxDynamicSharedMemorySize,
+                                 static_cast<int>(smem));
+    }();
+    if (attr != hipSuccess) return attr;
+  }
   a.S = (a.V + rows - 1) / rows;
-  const dim3 grid(a.S, (a.B + NT * 16 - 1) / (NT * 16));
+  const dim3 grid(a.S, (a.B + Loop::NT * 16 - 1) / (Loop::NT * 16));
   if (a.vocab_offset % 4 == 0)
-    fused_sample_kernel<MR, NT, NW, true><<<grid, NW * kWave, 0, stream>>>(a);
+    fused_sample_kernel<Loop, true><<<grid, Loop::NW * kWave, smem, stream>>>(a);
   else
-    fused_sample_kernel<MR, NT, NW, false><<<grid, NW * kWave, 0, stream>>>(a);
+    fused_sample_kernel<Loop, false><<<grid, Loop::NW * kWave, smem, stream>>>(a);
   return hipGetLastError();
+}
+
+template <class Loop>
+bool supports_cfg(int32_t D) {
+  return Loop::supports(D);
 }
 
 struct FusedConfig {
   const char* name;
   int rows_per_block;
   hipError_t (*launch)(SampleArgs&, hipStream_t);
+  bool (*supports)(int32_t D);
+  int order;  // configurations of equal order sum the contraction identically
 };
 
-#define FS_CFG(MR, NT, NW) \
-  {"direct_mr" #MR "_nt" #NT "_nw" #NW, MR * 16 * NW, &launch_cfg<MR, NT, NW>}
+template <class Loop>
+constexpr FusedConfig make_cfg(const char* name, int order) {
+  return {name, Loop::kRowsPerBlock, &launch_cfg<Loop>, &supports_cfg<Loop>, order};
+}
+
+#define FS_STREAM(MR, NT, NW, P, NTL) \
+  make_cfg<StreamLoop<MR, NT, NW, P, NTL>>("stream_mr" #MR "_nt" #NT "_nw" #NW "_p" #P "_ntl" #NTL, 0)
+#define FS_KSPLIT(MR, NT, NW, P, NTL) \
+  make_cfg<KSplitLoop<MR, NT, NW, P, NTL>>("ksplit_mr" #MR "_nt" #NT "_nw" #NW "_p" #P "_ntl" #NTL, NW)
+#define FS_LDS(MR, NT, NW, KC, AS, NTL)                                                          \
+  make_cfg<LdsLoop<MR, NT, NW, KC, AS, NTL>>(                                                  \
+      "lds_mr" #MR "_nt" #NT "_nw" #NW "_kc" #KC "_as" #AS "_ntl" #NTL, 0)
 
 const FusedConfig kConfigs[] = {
-    FS_CFG(4, 1, 4),   // 0: B <= 16
-    FS_CFG(4, 2, 4),   // 1: B <= 32
-    FS_CFG(2, 4, 4),   // 2: B <= 64
-    FS_CFG(1, 8, 4),   // 3: B <= 128
-    FS_CFG(1, 16, 4),  // 4: B > 128 (batch blocks of 256)
-    FS_CFG(2, 1, 4),   // 5: alternatives for tuning sweeps
-    FS_CFG(2, 2, 4),   // 6
+    FS_KSPLIT(1, 1, 4, 8, 0),        // 0  B <= 8
+    FS_LDS(2, 4, 4, 64, 2, 0),       // 1  B <= 64
+    FS_LDS(2, 8, 4, 64, 2, 0),       // 2  B <= 128
+    FS_LDS(2, 16, 4, 64, 2, 0),      // 3  B > 128 (batch blocks of 256)
+    FS_STREAM(4, 1, 4, 4, 0),        // 4  any D: fallback for B <= 16
+    FS_STREAM(2, 4, 4, 4, 0),        // 5  any D: fallback for larger B
+    // alternatives for tuning sweeps
+    FS_KSPLIT(2, 1, 4, 8, 0),
+    FS_KSPLIT(4, 1, 4, 4, 0),
+    FS_KSPLIT(2, 2, 4, 4, 0),
+    FS_KSPLIT(2, 2, 4, 8, 0),
+    FS_KSPLIT(4, 2, 4, 4, 0),
+    FS_KSPLIT(2, 4, 4, 4, 0),
+    FS_KSPLIT(1, 2, 4, 8, 0),
+    FS_KSPLIT(1, 1, 8, 8, 0),
+    FS_KSPLIT(1, 1, 4, 8, 1),
+    FS_STREAM(1, 1, 4, 8, 0),
+    FS_LDS(2, 8, 4, 64, 4, 0),
+    FS_LDS(4, 4, 4, 64, 4, 0),
+    FS_LDS(2, 16, 8, 64, 2, 0),
+    FS_LDS(2, 4, 4, 64, 2, 1),
+    FS_LDS(2, 16, 4, 64, 2, 1),
 };
-#undef FS_CFG
+#undef FS_STREAM
+#undef FS_KSPLIT
+#undef FS_LDS
 
 constexpr int kNumConfigs = sizeof(kConfigs) / sizeof(kConfigs[0]);
 
@@ -183,12 +246,22 @@ int fused_rows_per_block(int id) {
   return (id >= 0 && id < kNumConfigs) ? kConfigs[id].rows_per_block : 0;
 }
 
-int fused_auto_config(int32_t B, int32_t /*D*/, int32_t /*V*/) {
-  if (B <= 16) return 0;
-  if (B <= 32) return 1;
-  if (B <= 64) return 2;
-  if (B <= 128) return 3;
-  return 4;
+int fused_config_order(int id) {
+  return (id >= 0 && id < kNumConfigs) ? kConfigs[id].order : -1;
+}
+
+bool fused_config_supports(int id, int32_t D) {
+  return id >= 0 && id < kNumConfigs && kConfigs[id].supports(D);
+}
+
+int fused_auto_config(int32_t B, int32_t D, int32_t /*V*/) {
+  int id;
+  if (B <= 8) id = 0;
+  else if (B <= 64) id = 1;
+  else if (B <= 128) id = 2;
+  else id = 3;
+  if (kConfigs[id].supports(D)) return id;
+  return B <= 16 ? 4 : 5;
 }
 
 hipError_t launch_fused(int id, SampleArgs& a, hipStream_t stream) {

@@ -1,97 +1,291 @@
 // fs_mma.hpp -- the LM-head contraction tile on gfx950 bf16 MFMA.
 //
-// One wavefront computes a (MR*16 vocab rows) x (NT*16 batch rows) block of
-// logits z[b][v] = sum_d h[b][d] W[v][d] with v_mfma_f32_16x16x32_bf16:
-// W plays the MFMA "A" operand (rows = vocabulary), h the "B" operand
-// (columns = batch).  Operand fragments are read straight from global memory
-// into registers: every W element is used by exactly one wave, so staging W
-// through LDS would only add traffic; h is small and stays in L1/L2.
+// A wavefront computes (MR*16 vocabulary rows) x (NT*16 batch rows) of
+// logits z[b][v] = sum_d h[b][d] W[v][d] with v_mfma_f32_16x16x32_bf16: W is
+// the MFMA "A" operand (rows = vocabulary), h the "B" operand (columns =
+// batch).  Every W element is used by one wave only, so W fragments go
+// straight from global memory into registers; h, shared by all waves of a
+// block, is read through L1/L2 or staged in LDS.
 //
 // Register layouts (wave64, 16x16x32 bf16):
 //   A fragment, lane l: row (l % 16), 8 consecutive k at 8 * (l / 16)
 //   B fragment, lane l: col (l % 16), the same 8 k
 //   C tile,     lane l: col (l % 16), rows 4 * (l / 16) + {0,1,2,3}
-// A lane therefore loads 16 contiguous bytes of one W row per 32-wide k step,
-// and each lane ends up holding four consecutive vocabulary rows of one batch
-// row: exactly the four ids one Philox block covers.
+// A lane loads 16 contiguous bytes of one W row per 32-wide k step and ends up
+// holding four consecutive vocabulary rows of one batch row: exactly the four
+// ids one Philox block covers.
+//
+// Main-loop policies (all with the same interface, see fused_sample_kernel):
+//   StreamLoop  each wave owns MR*16 rows and the whole of D; both operands
+//               from global memory, P k-steps of loads in flight.
+//   KSplitLoop  the NW waves of a block share MR*16 rows and split D into NW
+//               slices; partial accumulators are summed through LDS in a
+//               fixed wave order.  Blocks are small and short-lived, so the
+//               rows being streamed at any moment form a narrow window of W,
+//               which keeps HBM row-buffer locality high (small batches).
+//   LdsLoop     each wave owns MR*16 rows; h is staged through LDS in
+//               KC-wide chunks (double-buffered, XOR-swizzled 16-byte pieces)
+//               and shared by the block's waves (large batches).
+// Rows >= V and batch rows >= B read clamped (valid) addresses; their results
+// are discarded by the epilogue, so operands need no masking except for the
+// k >= D tail of the stream loop.  W loads may use the non-temporal hint (NTL):
+// each W byte is read exactly once, so it should not displace h in the caches.
 #pragma once
 
 #include "fs_device.hpp"
 
 namespace fs {
 
+template <bool NTL = false>
 __device__ __forceinline__ bf16x8 load_frag(const __bf16* p) {
-  return __builtin_bit_cast(bf16x8, *reinterpret_cast<const u32x4*>(p));
+  const u32x4* q = reinterpret_cast<const u32x4*>(p);
+  return __builtin_bit_cast(bf16x8, NTL ? __builtin_nontemporal_load(q) : *q);
 }
 
 __device__ __forceinline__ bf16x8 zero_frag() {
   return __builtin_bit_cast(bf16x8, u32x4{0u, 0u, 0u, 0u});
 }
 
-// Accumulate the whole K = D contraction for one wave's block.
-//   W      [V][D] bf16, h [B][D] bf16
-//   row0   first vocabulary row of the block; rows >= V are clamped to V-1
-//          (their results are discarded by the caller)
-//   col0   first batch row; columns >= B read zeros
+__device__ __forceinline__ f32x4 mfma16(bf16x8 a, bf16x8 b, f32x4 c) {
+  return __builtin_amdgcn_mfma_f32_16x16x32_bf16(a, b, c, 0, 0, 0);
+}
+
 template <int MR, int NT>
-__device__ __forceinline__ void mma_block(const __bf16* __restrict__ W,
-                                          const __bf16* __restrict__ h, int32_t B,
-                                          int32_t D, int32_t V, int32_t row0, int32_t col0,
-                                          f32x4 (&acc)[MR][NT]) {
-  const int lane = threadIdx.x & (kWave - 1);
-  const int li = lane & 15, kb = lane >> 4;
+__device__ __forceinline__ void zero_acc(f32x4 (&acc)[MR][NT]) {
+  static_for<MR>([&](auto m) FS_INLINE {
+    static_for<NT>([&](auto n) FS_INLINE { acc[m][n] = f32x4{0.f, 0.f, 0.f, 0.f}; });
+  });
+}
 
-  const __bf16* arow[MR];
-#pragma unroll
-  for (int m = 0; m < MR; ++m) {
-    const int v = min(row0 + m * 16 + li, V - 1);
-    arow[m] = W + static_cast<size_t>(v) * D + 8 * kb;
-  }
-  const __bf16* brow[NT];
-  bool bvalid[NT];
-#pragma unroll
-  for (int n = 0; n < NT; ++n) {
-    const int b = col0 + n * 16 + li;
-    bvalid[n] = b < B;
-    brow[n] = h + static_cast<size_t>(min(b, B - 1)) * D + 8 * kb;
-  }
-#pragma unroll
-  for (int m = 0; m < MR; ++m)
-#pragma unroll
-    for (int n = 0; n < NT; ++n) acc[m][n] = f32x4{0.f, 0.f, 0.f, 0.f};
+// acc[m][n] += A[m] * B[n] for every (m, n) of the wave's block.
+template <int MR, int NT>
+__device__ __forceinline__ void mma_step(const bf16x8 (&a)[MR], const bf16x8 (&b)[NT],
+                                         f32x4 (&acc)[MR][NT]) {
+  static_for<MR>([&](auto m) FS_INLINE {
+    static_for<NT>([&](auto n) FS_INLINE { acc[m][n] = mfma16(a[m], b[n], acc[m][n]); });
+  });
+}
 
-  const int ksteps = D >> 5;
-#pragma unroll 4
-  for (int t = 0; t < ksteps; ++t) {
-    bf16x8 af[MR], bfr[NT];
-#pragma unroll
-    for (int m = 0; m < MR; ++m) af[m] = load_frag(arow[m] + t * 32);
-#pragma unroll
-    for (int n = 0; n < NT; ++n) {
-      const bf16x8 x = load_frag(brow[n] + t * 32);
-      bfr[n] = bvalid[n] ? x : zero_frag();
+// Pointers to the wave's A rows (clamped to V-1) and B rows (clamped to B-1),
+// each already offset to the lane's 8-element k piece and to k = kbeg.
+template <int MR, int NT>
+struct FragPtrs {
+  const __bf16* a[MR];
+  const __bf16* b[NT];
+  __device__ __forceinline__ FragPtrs(const __bf16* W, const __bf16* h, int32_t B, int32_t D,
+                                      int32_t V, int32_t row0, int32_t col0, int32_t kbeg) {
+    const int lane = threadIdx.x & (kWave - 1);
+    const int li = lane & 15, kb = lane >> 4;
+    static_for<MR>([&](auto m) FS_INLINE {
+      a[m] = W + static_cast<size_t>(min(row0 + m * 16 + li, V - 1)) * D + kbeg + 8 * kb;
+    });
+    static_for<NT>([&](auto n) FS_INLINE {
+      b[n] = h + static_cast<size_t>(min(col0 + n * 16 + li, B - 1)) * D + kbeg + 8 * kb;
+    });
+  }
+  template <bool NTL>
+  __device__ __forceinline__ void load(int t, bf16x8 (&af)[MR], bf16x8 (&bf)[NT]) const {
+    static_for<MR>([&](auto m) FS_INLINE { af[m] = load_frag<NTL>(a[m] + t * 32); });
+    static_for<NT>([&](auto n) FS_INLINE { bf[n] = load_frag<false>(b[n] + t * 32); });
+  }
+};
+
+// k-steps [0, ksteps) of one wave, P steps of loads in flight.  ksteps % P
+// steps at the end run unpipelined.
+template <int MR, int NT, int P, bool NTL>
+__device__ __forceinline__ void pipelined_ksteps(const FragPtrs<MR, NT>& ptr, int ksteps,
+                                                 f32x4 (&acc)[MR][NT]) {
+  const int kmain = ksteps - ksteps % P;
+  bf16x8 a[P][MR], b[P][NT];
+  if (kmain > 0) {
+    static_for<P>([&](auto p) FS_INLINE { ptr.template load<NTL>(p, a[p], b[p]); });
+    for (int t0 = P; t0 < kmain; t0 += P) {
+      static_for<P>([&](auto p) FS_INLINE {
+        mma_step(a[p], b[p], acc);
+        ptr.template load<NTL>(t0 + p, a[p], b[p]);
+      });
     }
-#pragma unroll
-    for (int m = 0; m < MR; ++m)
-#pragma unroll
-      for (int n = 0; n < NT; ++n)
-        acc[m][n] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(af[m], bfr[n], acc[m][n], 0, 0, 0);
+    static_for<P>([&](auto p) FS_INLINE { mma_step(a[p], b[p], acc); });
   }
-  if (D & 31) {  // last partial step: D % 8 == 0, so a lane's 8 k are all in or all out
-    const int k = ksteps * 32 + 8 * kb;
-    const bool kin = k < D;
+  for (int t = kmain; t < ksteps; ++t) {
     bf16x8 af[MR], bfr[NT];
-#pragma unroll
-    for (int m = 0; m < MR; ++m) af[m] = kin ? load_frag(arow[m] + ksteps * 32) : zero_frag();
-#pragma unroll
-    for (int n = 0; n < NT; ++n)
-      bfr[n] = (kin && bvalid[n]) ? load_frag(brow[n] + ksteps * 32) : zero_frag();
-#pragma unroll
-    for (int m = 0; m < MR; ++m)
-#pragma unroll
-      for (int n = 0; n < NT; ++n)
-        acc[m][n] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(af[m], bfr[n], acc[m][n], 0, 0, 0);
+    ptr.template load<NTL>(t, af, bfr);
+    mma_step(af, bfr, acc);
   }
 }
+
+// ---------------------------------------------------------------------------
+// StreamLoop
+// ---------------------------------------------------------------------------
+template <int MR_, int NT_, int NW_, int P, bool NTL>
+struct StreamLoop {
+  static constexpr int MR = MR_, NT = NT_, NW = NW_;
+  static constexpr int kRowsPerBlock = MR * 16 * NW;
+  static constexpr size_t kSmemBytes = 0;
+  static constexpr int kWavesPerSimd = 1;  // occupancy hint: none
+  static bool supports(int32_t /*D*/) { return true; }
+  __device__ __forceinline__ static int row0(int block, int wave) { return (block * NW + wave) * MR * 16; }
+  __device__ __forceinline__ static bool owns(int /*wave*/, int /*m*/, int /*n*/) { return true; }
+
+  __device__ __forceinline__ static void run(const __bf16* __restrict__ W, const __bf16* __restrict__ h,
+                             int32_t B, int32_t D, int32_t V, int32_t row0, int32_t col0,
+                             f32x4 (&acc)[MR][NT], void* /*smem*/) {
+    const FragPtrs<MR, NT> ptr(W, h, B, D, V, row0, col0, 0);
+    zero_acc(acc);
+    const int ksteps = D >> 5;
+    pipelined_ksteps<MR, NT, P, NTL>(ptr, ksteps, acc);
+    if (D & 31) {  // D % 8 == 0: a lane's 8 k are all inside or all outside
+      const int kb = (threadIdx.x & (kWave - 1)) >> 4;
+      const bool kin = ksteps * 32 + 8 * kb < D;
+      bf16x8 af[MR], bfr[NT];
+      static_for<MR>([&](auto m) FS_INLINE { af[m] = kin ? load_frag(ptr.a[m] + ksteps * 32) : zero_frag(); });
+      static_for<NT>([&](auto n) FS_INLINE { bfr[n] = kin ? load_frag(ptr.b[n] + ksteps * 32) : zero_frag(); });
+      mma_step(af, bfr, acc);
+    }
+  }
+};
+
+// ---------------------------------------------------------------------------
+// KSplitLoop: requires D % (32 * NW) == 0.
+// ---------------------------------------------------------------------------
+template <int MR_, int NT_, int NW_, int P, bool NTL>
+struct KSplitLoop {
+  static constexpr int MR = MR_, NT = NT_, NW = NW_;
+  static constexpr int kRowsPerBlock = MR * 16;
+  static constexpr size_t kSmemBytes = static_cast<size_t>(NW) * MR * NT * kWave * sizeof(f32x4);
+  static constexpr int kWavesPerSimd = 1;
+  static bool supports(int32_t D) { return D % (32 * NW) == 0; }
+  __device__ __forceinline__ static int row0(int block, int /*wave*/) { return block * MR * 16; }
+  // Tile (m, n) is finished (summed) by one wave; the others skip its epilogue.
+  __device__ __forceinline__ static bool owns(int wave, int m, int n) { return (m * NT + n) % NW == wave; }
+
+  __device__ __forceinline__ static void run(const __bf16* __restrict__ W, const __bf16* __restrict__ h,
+                             int32_t B, int32_t D, int32_t V, int32_t row0, int32_t col0,
+                             f32x4 (&acc)[MR][NT], void* smem) {
+    const int lane = threadIdx.x & (kWave - 1);
+    const int wave = threadIdx.x >> 6;
+    const int kw = D / NW;
+    const FragPtrs<MR, NT> ptr(W, h, B, D, V, row0, col0, wave * kw);
+    zero_acc(acc);
+    pipelined_ksteps<MR, NT, P, NTL>(ptr, kw >> 5, acc);
+
+    f32x4* red = static_cast<f32x4*>(smem);
+    static_for<MR>([&](auto m) FS_INLINE {
+      static_for<NT>([&](auto n) FS_INLINE { red[((wave * MR + m) * NT + n) * kWave + lane] = acc[m][n]; });
+    });
+    __syncthreads();
+    static_for<MR>([&](auto m) FS_INLINE {
+      static_for<NT>([&](auto n) FS_INLINE {
+        if (owns(wave, m, n)) {
+          f32x4 s = red[((0 * MR + m) * NT + n) * kWave + lane];
+          for (int w = 1; w < NW; ++w) s += red[((w * MR + m) * NT + n) * kWave + lane];
+          acc[m][n] = s;
+        }
+      });
+    });
+  }
+};
+
+// ---------------------------------------------------------------------------
+// LdsLoop: requires D % (KC * AS) == 0.
+// ---------------------------------------------------------------------------
+template <int MR_, int NT_, int NW_, int KC, int AS, bool NTL>
+struct LdsLoop {
+  static constexpr int MR = MR_, NT = NT_, NW = NW_;
+  static constexpr int kRowsPerBlock = MR * 16 * NW;
+  static constexpr int N = NT * 16;         // batch rows per block
+  static constexpr int KS = KC / 32;        // MFMA k-steps per chunk
+  static constexpr int CPR = KC / 8;        // 16-byte pieces per staged row
+  static constexpr int THREADS = NW * kWave;
+  static constexpr int LOADS = N * CPR / THREADS;  // staging loads per thread
+  static constexpr int STAGE = N * KC;      // bf16 elements per buffer
+  static constexpr size_t kSmemBytes = 2 * STAGE * sizeof(__bf16);
+  // Two waves per SIMD whenever the accumulators (MR*NT*4 registers) leave
+  // room: one wave's epilogue and barriers then overlap the other's MFMAs.
+  static constexpr int kWavesPerSimd = MR * NT * 4 <= 128 ? 2 : 1;
+  static_assert(N * CPR % THREADS == 0, "staging must divide evenly");
+  static_assert((CPR & (CPR - 1)) == 0, "KC/8 must be a power of two");
+  static bool supports(int32_t D) { return D % (KC * AS) == 0; }
+  __device__ __forceinline__ static int row0(int block, int wave) { return (block * NW + wave) * MR * 16; }
+  __device__ __forceinline__ static bool owns(int /*wave*/, int /*m*/, int /*n*/) { return true; }
+
+  // Piece j of staged row n lives at slot j ^ (n mod CPR): the 16 rows a
+  // B-fragment read touches at one k land in distinct bank groups.
+  __device__ __forceinline__ static int smem_off(int n, int j) { return n * KC + ((j ^ (n & (CPR - 1))) << 3); }
+
+  __device__ __forceinline__ static void stage_load(const __bf16* __restrict__ h, int32_t B, int32_t D,
+                                    int32_t col0, int c, u32x4 (&reg)[LOADS]) {
+    static_for<LOADS>([&](auto i) FS_INLINE {
+      const int idx = threadIdx.x + i * THREADS;
+      const int n = idx / CPR, j = idx % CPR;
+      const int b = min(col0 + n, B - 1);
+      reg[i] = *reinterpret_cast<const u32x4*>(h + static_cast<size_t>(b) * D + c * KC + j * 8);
+    });
+  }
+
+  __device__ __forceinline__ static void stage_store(__bf16* buf, const u32x4 (&reg)[LOADS]) {
+    static_for<LOADS>([&](auto i) FS_INLINE {
+      const int idx = threadIdx.x + i * THREADS;
+      const int n = idx / CPR, j = idx % CPR;
+      *reinterpret_cast<u32x4*>(buf + smem_off(n, j)) = reg[i];
+    });
+  }
+
+  __device__ __forceinline__ static void load_a(const __bf16* const (&arow)[MR], int c, bf16x8 (&a)[KS][MR]) {
+    static_for<KS>([&](auto s) FS_INLINE {
+      static_for<MR>([&](auto m) FS_INLINE { a[s][m] = load_frag<NTL>(arow[m] + c * KC + s * 32); });
+    });
+  }
+
+  __device__ __forceinline__ static void compute(const __bf16* buf, const bf16x8 (&a)[KS][MR],
+                                 f32x4 (&acc)[MR][NT]) {
+    const int lane = threadIdx.x & (kWave - 1);
+    const int li = lane & 15, kb = lane >> 4;
+    static_for<KS>([&](auto s) FS_INLINE {
+      static_for<NT>([&](auto n) FS_INLINE {
+        const bf16x8 bf = __builtin_bit_cast(
+            bf16x8, *reinterpret_cast<const u32x4*>(buf + smem_off(n * 16 + li, s * 4 + kb)));
+        static_for<MR>([&](auto m) FS_INLINE { acc[m][n] = mfma16(a[s][m], bf, acc[m][n]); });
+      });
+    });
+  }
+
+  __device__ __forceinline__ static void run(const __bf16* __restrict__ W, const __bf16* __restrict__ h,
+                             int32_t B, int32_t D, int32_t V, int32_t row0, int32_t col0,
+                             f32x4 (&acc)[MR][NT], void* smem) {
+    const int lane = threadIdx.x & (kWave - 1);
+    const int li = lane & 15, kb = lane >> 4;
+    __bf16* hs = static_cast<__bf16*>(smem);
+    const __bf16* arow[MR];
+    static_for<MR>([&](auto m) FS_INLINE {
+      arow[m] = W + static_cast<size_t>(min(row0 + m * 16 + li, V - 1)) * D + 8 * kb;
+    });
+    zero_acc(acc);
+
+    // nch is a multiple of AS (see supports), so the unrolled body below has
+    // no branch: every load is issued unconditionally, chunk indices past the
+    // end are clamped (their data is never used), and the in-order vmcnt
+    // accounting lets each chunk wait only for its own operands.
+    const int nch = D / KC;
+    u32x4 hreg[LOADS];
+    bf16x8 a[AS][KS][MR];
+    stage_load(h, B, D, col0, 0, hreg);
+    static_for<AS - 1>([&](auto s) FS_INLINE { load_a(arow, min(static_cast<int>(s), nch - 1), a[s]); });
+    stage_store(hs, hreg);
+    __syncthreads();
+
+    // chunk c uses register slot c % AS and LDS buffer c % 2
+    for (int c0 = 0; c0 < nch; c0 += AS) {
+      static_for<AS>([&](auto s) FS_INLINE {
+        const int c = c0 + s;
+        stage_load(h, B, D, col0, min(c + 1, nch - 1), hreg);
+        load_a(arow, min(c + AS - 1, nch - 1), a[(s + AS - 1) % AS]);
+        compute(hs + (c & 1) * STAGE, a[s], acc);
+        stage_store(hs + ((c + 1) & 1) * STAGE, hreg);  // after the last chunk: unused
+        __syncthreads();
+      });
+    }
+  }
+};
 
 }  // namespace fs

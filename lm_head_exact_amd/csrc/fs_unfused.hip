@@ -64,7 +64,7 @@ __global__ __launch_bounds__(NW * kWave) void gemm_logits_kernel(SampleArgs a, f
   const int row0 = (blockIdx.x * NW + wave) * (MR * 16);
   const int col0 = blockIdx.y * (NT * 16);
   f32x4 acc[MR][NT];
-  mma_block<MR, NT>(a.W, a.h, a.B, a.D, a.V, row0, col0, acc);
+  StreamLoop<MR, NT, NW, 4, false>::run(a.W, a.h, a.B, a.D, a.V, row0, col0, acc, nullptr);
 #pragma unroll
   for (int n = 0; n < NT; ++n) {
     const int b = col0 + n * 16 + li;
