@@ -77,16 +77,35 @@ __device__ __forceinline__ uint32_t pick_word(u32x4 w, uint32_t i) {
 }
 
 // Standard Gumbel value of a 32-bit word: u = (2k+1) 2^-24 with k the top 23
-// bits, g = -log(-log u).  The winners of a large vocabulary sit at u close
-// to 1 where -log u ~ 1 - u is tiny, so -log u is evaluated as
-// -log1p(-(1 - u)) from the complement 1 - u = (2^24 - 1 - 2k) 2^-24, which
-// is exact in fp32: the relative error of -log u stays at the library's few
-// ulp over the whole grid instead of growing as u -> 1.
+// bits, g = -ln(-ln u).
+//
+// Cost matters: this runs once per logit of the B x V tile, so it uses the
+// hardware base-2 logarithm (v_log_f32) instead of the library's
+// extended-precision logf/log1pf (about ten times the instructions).  The one
+// place the hardware log is not accurate enough is -ln u for u near 1, where
+// the winners of a large vocabulary sit (u ~ 1 - 1/V): there ln u is a small
+// difference and an absolute error in log2 becomes a large relative error in
+// -ln u, which the outer log turns into an absolute error in g.  Both u and
+// v = 1 - u = (2^24 - 1 - 2k) 2^-24 are exact in fp32, so for v <= 1/16 the
+// series -ln(1 - v) = v + v^2/2 + ... + v^7/7 (truncation below 5e-10
+// relative) is used instead.  Elsewhere |ln u| >= 0.06 and the hardware log
+// is used directly.  The device values are checked against the fp64 oracle
+// on all 2^23 grid points.
 __device__ __forceinline__ float gumbel_from_bits(uint32_t x) {
+  constexpr float kLn2 = 0.693147180559945309f;
   const uint32_t k = x >> 9;
-  const float one_minus_u = static_cast<float>(0xFFFFFFu - 2u * k) * 0x1p-24f;
-  const float e = -log1pf(-one_minus_u);  // -log u > 0
-  return -logf(e);
+  const float u = static_cast<float>(2u * k + 1u) * 0x1p-24f;
+  const float v = static_cast<float>(0xFFFFFFu - 2u * k) * 0x1p-24f;
+  float series = 1.0f / 7.0f;
+  series = __builtin_fmaf(series, v, 1.0f / 6.0f);
+  series = __builtin_fmaf(series, v, 1.0f / 5.0f);
+  series = __builtin_fmaf(series, v, 1.0f / 4.0f);
+  series = __builtin_fmaf(series, v, 1.0f / 3.0f);
+  series = __builtin_fmaf(series, v, 1.0f / 2.0f);
+  series = __builtin_fmaf(series, v, 1.0f);
+  series *= v;
+  const float neg_ln_u = v <= 0.0625f ? series : -__builtin_amdgcn_logf(u) * kLn2;
+  return -__builtin_amdgcn_logf(neg_ln_u) * kLn2;
 }
 
 // ---------------------------------------------------------------------------
@@ -108,6 +127,13 @@ struct ArgMax {
       v = nv;
       i = ni;
     }
+  }
+  // Push for ids that arrive in increasing order: a strict '>' already keeps
+  // the smaller id on a tie.
+  __device__ __forceinline__ void push_ascending(float nv, int32_t ni) {
+    const bool gt = nv > v;
+    v = gt ? nv : v;
+    i = gt ? ni : i;
   }
   // Combine with the pair held by lane (lane ^ mask).
   __device__ __forceinline__ void xor_reduce(int mask) {

@@ -69,7 +69,7 @@ __attribute__((amdgpu_waves_per_eu(Loop::kWavesPerSimd))) void fused_sample_kern
                 }
                 s = perturbed_score(s, inv_t, gumbel_from_bits(x));
               }
-              best[n].push(s, static_cast<int32_t>(gv));
+              best[n].push_ascending(s, static_cast<int32_t>(gv));  // gv grows with (m, r)
             }
           });
         }
