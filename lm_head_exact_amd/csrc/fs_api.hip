@@ -106,9 +106,9 @@ fs_status run_fused(const void* h, const void* W, int32_t B, int32_t D, int32_t 
     return fail(FS_ERR_WORKSPACE, "%s: workspace of %zu bytes is below the %zu required", who,
                 workspace_bytes, need);
   const int cfg = choose_config(B, D, V);
-  if (!fs::fused_config_supports(cfg, D))
-    return fail(FS_ERR_UNSUPPORTED, "%s: forced configuration %s does not support D=%d", who,
-                fs::fused_config_name(cfg), D);
+  if (!fs::fused_config_supports(cfg, B, D))
+    return fail(FS_ERR_UNSUPPORTED, "%s: forced configuration %s does not support B=%d, D=%d",
+                who, fs::fused_config_name(cfg), B, D);
   const size_t S = (static_cast<size_t>(V) + fs::kMinRowsPerBlock - 1) / fs::kMinRowsPerBlock;
   fs::SampleArgs a;
   a.h = static_cast<const __bf16*>(h);

@@ -104,6 +104,139 @@ __attribute__((amdgpu_waves_per_eu(Loop::kWavesPerSimd))) void fused_sample_kern
   }
 }
 
+// ---------------------------------------------------------------------------
+// Persistent K-split sampler for small batches (NT * 16 batch rows).
+//
+// Block = NW waves, one or two per SIMD, launched once per CU slot.  Wave w
+// owns the D-slice [w*KS*32, (w+1)*KS*32) and keeps h for that slice in
+// registers for the whole kernel, so h is read from memory once per block.
+// Blocks sweep the 16-row vocabulary groups g = block, block + G, ...: the
+// groups being streamed at any moment form a narrow moving window of W,
+// which keeps HBM row-buffer locality high.  W fragments stream through a
+// P-deep register ring that runs ahead across group boundaries.  After each
+// group the NW partial accumulators are summed through LDS (two buffers,
+// fixed wave order) by one owner wave per batch tile, which runs the
+// epilogue; ownership rotates over the waves.  The running (max, argmax)
+// persists across groups, so a block emits one partial per batch row.
+// Requires D == 32 * NW * KS.
+// ---------------------------------------------------------------------------
+template <int NT, int NW, int KS, int P, bool ALIGN4>
+__global__ __launch_bounds__(NW * kWave) void persist_sample_kernel(SampleArgs a) {
+  static_assert(KS % P == 0, "the load ring must tile a group");
+  extern __shared__ __attribute__((aligned(16))) unsigned char dyn_smem[];
+  f32x4* red = reinterpret_cast<f32x4*>(dyn_smem);  // [2][NW][NT][kWave]
+  const int lane = threadIdx.x & (kWave - 1);
+  const int wave = threadIdx.x >> 6;
+  const int li = lane & 15, kb = lane >> 4;
+  const int D = a.D;
+  const int kbeg = wave * KS * 32 + 8 * kb;
+  const int ngroups = (a.V + 15) / 16;
+  const int G = gridDim.x;
+
+  bf16x8 hreg[KS][NT];
+  bool bvalid[NT], greedy[NT];
+  float inv_t[NT];
+  static_for<NT>([&](auto n) FS_INLINE {
+    const int b = n * 16 + li;
+    bvalid[n] = b < a.B;
+    const __bf16* hp = a.h + static_cast<size_t>(min(b, a.B - 1)) * D + kbeg;
+    static_for<KS>([&](auto s) FS_INLINE { hreg[s][n] = load_frag(hp + s * 32); });
+    const float T = bvalid[n] ? a.temperature[b] : 1.0f;
+    greedy[n] = row_is_greedy(T);
+    inv_t[n] = row_inv_temperature(T);
+  });
+
+  auto group_ptr = [&](int g) FS_INLINE {
+    return a.W + static_cast<size_t>(min(min(g, ngroups - 1) * 16 + li, a.V - 1)) * D + kbeg;
+  };
+  const Philox philox(a.seed);
+  ArgMax best[NT];
+  static_for<NT>([&](auto n) FS_INLINE { best[n].init(); });
+
+  int g = blockIdx.x;
+  const __bf16* ap = group_ptr(g);
+  const __bf16* ap_next = group_ptr(g + G);
+  bf16x8 ring[P];
+  static_for<P>([&](auto p) FS_INLINE { ring[p] = load_frag(ap + p * 32); });
+
+  for (int it = 0; g < ngroups; g += G, ++it) {
+    f32x4 acc[NT];
+    static_for<NT>([&](auto n) FS_INLINE { acc[n] = f32x4{0.f, 0.f, 0.f, 0.f}; });
+    static_for<KS>([&](auto sc) FS_INLINE {
+      constexpr int s = decltype(sc)::value;
+      constexpr int slot = s % P;
+      static_for<NT>([&](auto n) FS_INLINE { acc[n] = mfma16(ring[slot], hreg[s][n], acc[n]); });
+      // refill with the k-step P ahead (the next group's, past the end of this one)
+      if constexpr (s + P < KS)
+        ring[slot] = load_frag(ap + (s + P) * 32);
+      else
+        ring[slot] = load_frag(ap_next + (s + P - KS) * 32);
+    });
+    ap = ap_next;
+    ap_next = group_ptr(g + 2 * G);
+
+    const int par = it & 1;
+    static_for<NT>([&](auto n) FS_INLINE {
+      red[((par * NW + wave) * NT + n) * kWave + lane] = acc[n];
+    });
+    __syncthreads();
+    static_for<NT>([&](auto n) FS_INLINE {
+      if ((n + it) % NW == wave && bvalid[n]) {
+        f32x4 z = red[((par * NW + 0) * NT + n) * kWave + lane];
+        for (int w = 1; w < NW; ++w) z += red[((par * NW + w) * NT + n) * kWave + lane];
+        const int b = n * 16 + li;
+        const int v0 = g * 16 + 4 * kb;
+        const uint32_t gv0 = static_cast<uint32_t>(a.vocab_offset + v0);
+        u32x4 w0 = u32x4{0u, 0u, 0u, 0u}, w1 = w0;
+        if (!greedy[n]) {
+          w0 = philox(noise_counter(gv0, b, a.step));
+          if (!ALIGN4) w1 = philox(noise_counter(gv0 + 4u, b, a.step));
+        }
+        static_for<4>([&](auto rc) FS_INLINE {
+          constexpr int r = decltype(rc)::value;
+          if (v0 + r < a.V) {
+            float sc = z[r];
+            if (!greedy[n]) {
+              uint32_t x;
+              if (ALIGN4) {
+                x = w0[r];
+              } else {
+                const uint32_t q = (gv0 & 3u) + r;
+                x = q < 4u ? pick_word(w0, q) : pick_word(w1, q - 4u);
+              }
+              sc = perturbed_score(sc, inv_t[n], gumbel_from_bits(x));
+            }
+            best[n].push_ascending(sc, static_cast<int32_t>(gv0 + r));  // g grows per owner
+          }
+        });
+      }
+    });
+  }
+
+  static_for<NT>([&](auto n) FS_INLINE {
+    best[n].xor_reduce(16);
+    best[n].xor_reduce(32);
+  });
+  __shared__ float s_val[NW][NT * 16];
+  __shared__ int32_t s_idx[NW][NT * 16];
+  if (kb == 0) {
+    static_for<NT>([&](auto n) FS_INLINE {
+      s_val[wave][n * 16 + li] = best[n].v;
+      s_idx[wave][n * 16 + li] = best[n].i;
+    });
+  }
+  __syncthreads();
+  for (int c = threadIdx.x; c < NT * 16 && c < a.B; c += NW * kWave) {
+    ArgMax m;
+    m.init();
+#pragma unroll
+    for (int w = 0; w < NW; ++w) m.push(s_val[w][c], s_idx[w][c]);
+    const size_t o = static_cast<size_t>(c) * a.S + blockIdx.x;
+    a.part_val[o] = m.v;
+    a.part_idx[o] = m.i;
+  }
+}
+
 // One wave per batch row: argmax over P (value, id) pairs.
 __global__ __launch_bounds__(256) void merge_kernel(const float* __restrict__ val,
                                                     const int32_t* __restrict__ idx,
@@ -179,21 +312,67 @@ hipError_t launch_cfg(SampleArgs& a, hipStream_t stream) {
 }
 
 template <class Loop>
-bool supports_cfg(int32_t D) {
+bool supports_cfg(int32_t /*B*/, int32_t D) {
   return Loop::supports(D);
 }
+
+// Blocks of `kernel` that fit on one CU, times the CU count of the current
+// device (cached per device).
+template <class Kernel>
+int resident_blocks(Kernel kernel, int threads, size_t smem) {
+  static int cached_dev = -1, cached = 0;
+  int dev = 0;
+  if (hipGetDevice(&dev) != hipSuccess) return 0;
+  if (dev != cached_dev) {
+    int cus = 0, per_cu = 0;
+    if (hipDeviceGetAttribute(&cus, hipDeviceAttributeMultiprocessorCount, dev) != hipSuccess ||
+        hipOccupancyMaxActiveBlocksPerMultiprocessor(&per_cu, kernel, threads, smem) !=
+            hipSuccess)
+      return 0;
+    cached = cus * (per_cu > 0 ? per_cu : 1);
+    cached_dev = dev;
+  }
+  return cached;
+}
+
+template <int NT, int NW, int KS, int P>
+struct Persist {
+  static constexpr size_t kSmemBytes = 2ull * NW * NT * kWave * sizeof(f32x4);
+  static bool supports(int32_t B, int32_t D) { return B <= NT * 16 && D == 32 * NW * KS; }
+  static hipError_t launch(SampleArgs& a, hipStream_t stream) {
+    if (!supports(a.B, a.D)) return hipErrorInvalidValue;
+    const int ngroups = (a.V + 15) / 16;
+    const bool al4 = a.vocab_offset % 4 == 0;
+    const int slots = al4 ? resident_blocks(persist_sample_kernel<NT, NW, KS, P, true>,
+                                            NW * kWave, kSmemBytes)
+                          : resident_blocks(persist_sample_kernel<NT, NW, KS, P, false>,
+                                            NW * kWave, kSmemBytes);
+    if (slots <= 0) return hipErrorInvalidDevice;
+    a.S = ngroups < slots ? ngroups : slots;
+    if (al4)
+      persist_sample_kernel<NT, NW, KS, P, true><<<a.S, NW * kWave, kSmemBytes, stream>>>(a);
+    else
+      persist_sample_kernel<NT, NW, KS, P, false><<<a.S, NW * kWave, kSmemBytes, stream>>>(a);
+    return hipGetLastError();
+  }
+};
 
 struct FusedConfig {
   const char* name;
   int rows_per_block;
   hipError_t (*launch)(SampleArgs&, hipStream_t);
-  bool (*supports)(int32_t D);
+  bool (*supports)(int32_t B, int32_t D);
   int order;  // configurations of equal order sum the contraction identically
 };
 
 template <class Loop>
 constexpr FusedConfig make_cfg(const char* name, int order) {
   return {name, Loop::kRowsPerBlock, &launch_cfg<Loop>, &supports_cfg<Loop>, order};
+}
+
+template <class Pol>
+constexpr FusedConfig make_persist(const char* name, int order) {
+  return {name, 16, &Pol::launch, &Pol::supports, order};
 }
 
 #define FS_STREAM(MR, NT, NW, P, NTL) \
@@ -203,6 +382,8 @@ constexpr FusedConfig make_cfg(const char* name, int order) {
 #define FS_LDS(MR, NT, NW, KC, AS, NTL)                                                          \
   make_cfg<LdsLoop<MR, NT, NW, KC, AS, NTL>>(                                                  \
       "lds_mr" #MR "_nt" #NT "_nw" #NW "_kc" #KC "_as" #AS "_ntl" #NTL, 0)
+#define FS_PERSIST(NT, NW, KS, P) \
+  make_persist<Persist<NT, NW, KS, P>>("persist_nt" #NT "_nw" #NW "_ks" #KS "_p" #P, 100 + NW)
 
 const FusedConfig kConfigs[] = {
     FS_KSPLIT(1, 1, 4, 8, 0),        // 0  B <= 8
@@ -211,7 +392,14 @@ const FusedConfig kConfigs[] = {
     FS_LDS(2, 16, 4, 64, 2, 0),      // 3  B > 128 (batch blocks of 256)
     FS_STREAM(4, 1, 4, 4, 0),        // 4  any D: fallback for B <= 16
     FS_STREAM(2, 4, 4, 4, 0),        // 5  any D: fallback for larger B
+    FS_PERSIST(1, 8, 16, 8),         // 6  D = 4096, B <= 16
+    FS_PERSIST(2, 8, 16, 8),         // 7  D = 4096, B <= 32
+    FS_PERSIST(1, 8, 32, 8),         // 8  D = 8192, B <= 16
+    FS_PERSIST(1, 4, 2, 2),          // 9  D = 256 (small shapes)
+    FS_PERSIST(2, 4, 2, 2),          // 10 D = 256
     // alternatives for tuning sweeps
+    FS_PERSIST(1, 8, 16, 16),
+    FS_PERSIST(2, 8, 16, 4),
     FS_KSPLIT(2, 1, 4, 8, 0),
     FS_KSPLIT(4, 1, 4, 4, 0),
     FS_KSPLIT(2, 2, 4, 4, 0),
@@ -231,6 +419,7 @@ const FusedConfig kConfigs[] = {
 #undef FS_STREAM
 #undef FS_KSPLIT
 #undef FS_LDS
+#undef FS_PERSIST
 
 constexpr int kNumConfigs = sizeof(kConfigs) / sizeof(kConfigs[0]);
 
@@ -250,17 +439,20 @@ int fused_config_order(int id) {
   return (id >= 0 && id < kNumConfigs) ? kConfigs[id].order : -1;
 }
 
-bool fused_config_supports(int id, int32_t D) {
-  return id >= 0 && id < kNumConfigs && kConfigs[id].supports(D);
+bool fused_config_supports(int id, int32_t B, int32_t D) {
+  return id >= 0 && id < kNumConfigs && kConfigs[id].supports(B, D);
 }
 
 int fused_auto_config(int32_t B, int32_t D, int32_t /*V*/) {
+  // persistent K-split where h fits in registers, else by batch size
+  for (int id : {6, 7, 8})
+    if (kConfigs[id].supports(B, D)) return id;
   int id;
   if (B <= 8) id = 0;
   else if (B <= 64) id = 1;
   else if (B <= 128) id = 2;
   else id = 3;
-  if (kConfigs[id].supports(D)) return id;
+  if (kConfigs[id].supports(B, D)) return id;
   return B <= 16 ? 4 : 5;
 }
 

@@ -24,7 +24,7 @@ int num_fused_configs();
 const char* fused_config_name(int id);
 int fused_rows_per_block(int id);
 int fused_auto_config(int32_t B, int32_t D, int32_t V);
-bool fused_config_supports(int id, int32_t D);
+bool fused_config_supports(int id, int32_t B, int32_t D);
 // Configurations with equal order sum each logit's products identically.
 int fused_config_order(int id);
 // Smallest rows-per-block over all configurations: bounds the split count.
