@@ -55,6 +55,42 @@ def flops(B, D, V):
     return 2 * B * V * D
 
 
+TRAFFIC_PROFILE = os.path.join(ROOT, "profiles", "fused_sample_llama3_b32_hbm_traffic.txt")
+
+
+def kernel_sources_sha256():
+    """Fingerprint of the HIP sources: counters taken on other sources no
+    longer describe the kernel that runs."""
+    import hashlib
+    csrc = os.path.join(ROOT, "lm_head_exact_amd", "csrc")
+    h = hashlib.sha256()
+    for name in sorted(os.listdir(csrc)):
+        if name.endswith((".hip", ".hpp")):
+            h.update(name.encode())
+            h.update(open(os.path.join(csrc, name), "rb").read())
+    return h.hexdigest()
+
+
+def measured_traffic(B):
+    """HBM bytes per launch of the fused kernel (read + written) from the
+    committed rocprofv3 FETCH_SIZE / WRITE_SIZE summary, calibrated against a
+    copy of known size; None when absent, taken at another batch size, or
+    taken on different kernel sources."""
+    try:
+        kv = {}
+        for line in open(TRAFFIC_PROFILE):
+            if "=" in line and not line.lstrip().startswith("#"):
+                k, v = line.split("=", 1)
+                kv[k.strip()] = v.strip()
+        if kv.get("kernel_sources_sha256") != kernel_sources_sha256():
+            return None
+        if int(kv.get("batch", -1)) != B:
+            return None
+        return int(float(kv["hbm_bytes_per_launch"]))
+    except (OSError, KeyError, ValueError):
+        return None
+
+
 def roofline_us(B, D, V):
     return max(algorithmic_bytes(B, D, V) / (HBM_PEAK_GBS * 1e3),
                flops(B, D, V) / (MFMA_BF16_PEAK_TFLOPS * 1e6))
@@ -153,7 +189,8 @@ def main():
         t = time_steps(torch, f, args.sweep_steps, 10, stream) * 1e3
         kt, _, _, _ = measure_fused_kernel(torch, fsl, f, args.sweep_steps, 5)
         kt *= 1e3
-        entry = {"B": b, "us_per_step": round(t, 2), "kernel_us": round(kt, 2),
+        entry = {"B": b, "config": fsl.config_name(fsl.selected_config(b, D, V)),
+                 "us_per_step": round(t, 2), "kernel_us": round(kt, 2),
                  "roofline_us": round(roofline_us(b, D, V), 2),
                  "frac_of_roofline": round(roofline_us(b, D, V) / t, 4),
                  "kernel_hbm_GBs": round(algorithmic_bytes(b, D, V) / (kt * 1e3), 1),
@@ -199,7 +236,9 @@ def main():
         "frac_of_roofline": round(roofline_us(B, D, V) / us, 4),
         "roofline": {"bound": "hbm", "achieved": round(achieved_gbs, 1), "peak": HBM_PEAK_GBS,
                      "unit": "GB/s", "frac": round(achieved_gbs / HBM_PEAK_GBS, 4),
-                     "traffic": None, "kernel": "fused_sample_kernel",
+                     "traffic": measured_traffic(B),
+                     "kernel": fsl.config_name(fsl.selected_config(B, D, V)),
+                     "kernel_sources_sha256": kernel_sources_sha256()[:16],
                      "kernel_avg_us": round(k_us, 2), "kernel_min_us": round(k_lo * 1e3, 2),
                      "kernel_max_us": round(k_hi * 1e3, 2), "kernel_launches": k_n,
                      "algorithmic_bytes_per_launch": bytes_},
