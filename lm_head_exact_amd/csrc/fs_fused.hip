@@ -26,10 +26,11 @@ __attribute__((amdgpu_waves_per_eu(Loop::kWavesPerSimd))) void fused_sample_kern
   const int wave = threadIdx.x >> 6;
   const int li = lane & 15, kb = lane >> 4;
   const int row0 = Loop::row0(blockIdx.x, wave);
-  const int col0 = blockIdx.y * (NT * 16);
+  const int block_col0 = blockIdx.y * Loop::kBlockCols;
 
   f32x4 acc[MR][NT];
-  Loop::run(a.W, a.h, a.B, a.D, a.V, row0, col0, acc, dyn_smem);
+  Loop::run(a.W, a.h, a.B, a.D, a.V, row0, block_col0, acc, dyn_smem);
+  const int col0 = block_col0 + Loop::col_off(wave);  // this wave's first batch row
 
   // ---- epilogue: scale, perturb, running (max, argmax) per batch row ----
   // Lane (li, kb) holds batch row col0 + 16n + li and vocabulary rows
@@ -91,13 +92,15 @@ __attribute__((amdgpu_waves_per_eu(Loop::kWavesPerSimd))) void fused_sample_kern
     });
   }
   __syncthreads();
-  for (int c = threadIdx.x; c < NT * 16; c += NW * kWave) {
-    const int b = col0 + c;
+  // block column c is covered by the waves w with col_off(w) == c - c % (NT*16)
+  for (int c = threadIdx.x; c < Loop::kBlockCols; c += NW * kWave) {
+    const int b = block_col0 + c;
     if (b >= a.B) break;
     ArgMax m;
     m.init();
 #pragma unroll
-    for (int w = 0; w < NW; ++w) m.push(s_val[w][c], s_idx[w][c]);
+    for (int w = 0; w < NW; ++w)
+      if (Loop::col_off(w) == c - c % (NT * 16)) m.push(s_val[w][c % (NT * 16)], s_idx[w][c % (NT * 16)]);
     const size_t o = static_cast<size_t>(b) * a.S + blockIdx.x;
     a.part_val[o] = m.v;
     a.part_idx[o] = m.i;
@@ -303,7 +306,7 @@ hipError_t launch_cfg(SampleArgs& a, hipStream_t stream) {
     if (attr != hipSuccess) return attr;
   }
   a.S = (a.V + rows - 1) / rows;
-  const dim3 grid(a.S, (a.B + Loop::NT * 16 - 1) / (Loop::NT * 16));
+  const dim3 grid(a.S, (a.B + Loop::kBlockCols - 1) / Loop::kBlockCols);
   if (a.vocab_offset % 4 == 0)
     fused_sample_kernel<Loop, true><<<grid, Loop::NW * kWave, smem, stream>>>(a);
   else
@@ -379,17 +382,23 @@ constexpr FusedConfig make_persist(const char* name, int order) {
   make_cfg<StreamLoop<MR, NT, NW, P, NTL>>("stream_mr" #MR "_nt" #NT "_nw" #NW "_p" #P "_ntl" #NTL, 0)
 #define FS_KSPLIT(MR, NT, NW, P, NTL) \
   make_cfg<KSplitLoop<MR, NT, NW, P, NTL>>("ksplit_mr" #MR "_nt" #NT "_nw" #NW "_p" #P "_ntl" #NTL, NW)
-#define FS_LDS(MR, NT, NW, KC, AS, NTL)                                                          \
-  make_cfg<LdsLoop<MR, NT, NW, KC, AS, NTL>>(                                                  \
-      "lds_mr" #MR "_nt" #NT "_nw" #NW "_kc" #KC "_as" #AS "_ntl" #NTL, 0)
+#define FS_LDS(MR, NT, NW, KC, P, NTL)                                                           \
+  make_cfg<LdsLoop<MR, NT, NW, KC, P, NTL>>(                                                   \
+      "lds_mr" #MR "_nt" #NT "_nw" #NW "_kc" #KC "_p" #P "_ntl" #NTL, 0)
+#define FS_LDSB(MR, NT, NW, KC, P, WB)                                                         \
+  make_cfg<LdsLoop<MR, NT, NW, KC, P, false, WB>>(                                             \
+      "lds_mr" #MR "_nt" #NT "_nw" #NW "_kc" #KC "_p" #P "_wb" #WB, 0)
+#define FS_LDSR(MR, NT, NW, KC, P, WB, BR)                                                     \
+  make_cfg<LdsLoop<MR, NT, NW, KC, P, false, WB, BR>>(                                         \
+      "lds_mr" #MR "_nt" #NT "_nw" #NW "_kc" #KC "_p" #P "_wb" #WB "_br" #BR, 0)
 #define FS_PERSIST(NT, NW, KS, P) \
   make_persist<Persist<NT, NW, KS, P>>("persist_nt" #NT "_nw" #NW "_ks" #KS "_p" #P, 100 + NW)
 
 const FusedConfig kConfigs[] = {
-    FS_KSPLIT(1, 1, 4, 8, 0),        // 0  B <= 8
-    FS_LDS(2, 4, 4, 64, 2, 0),       // 1  B <= 64
-    FS_LDS(2, 8, 4, 64, 2, 0),       // 2  B <= 128
-    FS_LDS(2, 16, 4, 64, 2, 0),      // 3  B > 128 (batch blocks of 256)
+    FS_KSPLIT(1, 1, 4, 8, 0),        // 0  B <= 8 when no persistent shape fits
+    FS_LDS(2, 4, 4, 64, 8, 0),       // 1  B <= 64
+    FS_LDS(2, 8, 4, 64, 8, 0),       // 2  B <= 128
+    FS_LDS(2, 16, 4, 64, 4, 0),      // 3  B > 128 (batch blocks of 256)
     FS_STREAM(4, 1, 4, 4, 0),        // 4  any D: fallback for B <= 16
     FS_STREAM(2, 4, 4, 4, 0),        // 5  any D: fallback for larger B
     FS_PERSIST(1, 8, 16, 8),         // 6  D = 4096, B <= 16
@@ -399,27 +408,33 @@ const FusedConfig kConfigs[] = {
     FS_PERSIST(2, 4, 2, 2),          // 10 D = 256
     // alternatives for tuning sweeps
     FS_PERSIST(1, 8, 16, 16),
-    FS_PERSIST(2, 8, 16, 4),
-    FS_KSPLIT(2, 1, 4, 8, 0),
-    FS_KSPLIT(4, 1, 4, 4, 0),
-    FS_KSPLIT(2, 2, 4, 4, 0),
-    FS_KSPLIT(2, 2, 4, 8, 0),
-    FS_KSPLIT(4, 2, 4, 4, 0),
-    FS_KSPLIT(2, 4, 4, 4, 0),
-    FS_KSPLIT(1, 2, 4, 8, 0),
-    FS_KSPLIT(1, 1, 8, 8, 0),
-    FS_KSPLIT(1, 1, 4, 8, 1),
-    FS_STREAM(1, 1, 4, 8, 0),
-    FS_LDS(2, 8, 4, 64, 4, 0),
+    FS_LDS(2, 4, 4, 64, 4, 0),
     FS_LDS(4, 4, 4, 64, 4, 0),
-    FS_LDS(2, 16, 8, 64, 2, 0),
-    FS_LDS(2, 4, 4, 64, 2, 1),
-    FS_LDS(2, 16, 4, 64, 2, 1),
+    FS_LDS(4, 4, 4, 64, 8, 0),
+    FS_LDS(2, 8, 4, 64, 4, 0),
+    FS_LDS(4, 8, 4, 64, 4, 0),
+    FS_LDS(2, 16, 4, 64, 2, 0),
+    FS_LDS(2, 16, 8, 64, 4, 0),
+    FS_LDSB(4, 8, 8, 64, 4, 2),
+    FS_LDSR(2, 16, 4, 64, 2, 1, 4),
+    FS_LDSR(2, 16, 4, 64, 2, 1, 6),
+    FS_LDSR(2, 16, 4, 64, 4, 1, 4),
+    FS_LDSR(4, 8, 4, 64, 4, 1, 4),
+    FS_LDSR(2, 8, 4, 64, 8, 1, 4),
+    FS_LDSR(2, 4, 4, 64, 8, 1, 4),
+    FS_LDSR(4, 8, 8, 64, 4, 2, 4),
+    FS_LDSR(4, 16, 4, 64, 4, 1, 4),
+    FS_LDSR(4, 16, 4, 64, 2, 1, 4),
+    FS_KSPLIT(2, 1, 4, 8, 0),
+    FS_KSPLIT(4, 2, 4, 4, 0),
+    FS_STREAM(1, 1, 4, 8, 0),
 };
 #undef FS_STREAM
 #undef FS_KSPLIT
 #undef FS_LDS
 #undef FS_PERSIST
+#undef FS_LDSB
+#undef FS_LDSR
 
 constexpr int kNumConfigs = sizeof(kConfigs) / sizeof(kConfigs[0]);
 

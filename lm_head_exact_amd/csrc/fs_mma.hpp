@@ -124,7 +124,9 @@ struct StreamLoop {
   static constexpr size_t kSmemBytes = 0;
   static constexpr int kWavesPerSimd = 1;  // occupancy hint: none
   static bool supports(int32_t /*D*/) { return true; }
+  static constexpr int kBlockCols = NT * 16;
   __device__ __forceinline__ static int row0(int block, int wave) { return (block * NW + wave) * MR * 16; }
+  __device__ __forceinline__ static int col_off(int /*wave*/) { return 0; }
   __device__ __forceinline__ static bool owns(int /*wave*/, int /*m*/, int /*n*/) { return true; }
 
   __device__ __forceinline__ static void run(const __bf16* __restrict__ W, const __bf16* __restrict__ h,
@@ -155,7 +157,9 @@ struct KSplitLoop {
   static constexpr size_t kSmemBytes = static_cast<size_t>(NW) * MR * NT * kWave * sizeof(f32x4);
   static constexpr int kWavesPerSimd = 1;
   static bool supports(int32_t D) { return D % (32 * NW) == 0; }
+  static constexpr int kBlockCols = NT * 16;
   __device__ __forceinline__ static int row0(int block, int /*wave*/) { return block * MR * 16; }
+  __device__ __forceinline__ static int col_off(int /*wave*/) { return 0; }
   // Tile (m, n) is finished (summed) by one wave; the others skip its epilogue.
   __device__ __forceinline__ static bool owns(int wave, int m, int n) { return (m * NT + n) % NW == wave; }
 
@@ -187,34 +191,56 @@ struct KSplitLoop {
 };
 
 // ---------------------------------------------------------------------------
-// LdsLoop: requires D % (KC * AS) == 0.
+// LdsLoop: h staged through LDS in KC-wide chunks; W fragments stream through
+// a ring of P k-steps that runs ahead of the MFMAs across chunk boundaries.
+// Requires D % (KC * U) == 0 with U the chunk unroll below.
 // ---------------------------------------------------------------------------
-template <int MR_, int NT_, int NW_, int KC, int AS, bool NTL>
+template <int MR_, int NT_, int NW_, int KC, int P, bool NTL, int WB_ = 1, int BR = 0>
 struct LdsLoop {
   static constexpr int MR = MR_, NT = NT_, NW = NW_;
-  static constexpr int kRowsPerBlock = MR * 16 * NW;
-  static constexpr int N = NT * 16;         // batch rows per block
+  // The block's waves form WR row groups x WB batch groups: with WB > 1 each
+  // W row group is computed by WB waves against different batch rows, which
+  // halves (WB = 2) the LDS bytes read per MFMA for the same accumulators.
+  static constexpr int WB = WB_, WR = NW / WB;
+  static_assert(NW % WB == 0, "waves must tile the block");
+  static constexpr int kRowsPerBlock = MR * 16 * WR;
+  static constexpr int kBlockCols = NT * 16 * WB;
+  static constexpr int N = kBlockCols;      // batch rows per block (staged in LDS)
   static constexpr int KS = KC / 32;        // MFMA k-steps per chunk
   static constexpr int CPR = KC / 8;        // 16-byte pieces per staged row
   static constexpr int THREADS = NW * kWave;
   static constexpr int LOADS = N * CPR / THREADS;  // staging loads per thread
   static constexpr int STAGE = N * KC;      // bf16 elements per buffer
   static constexpr size_t kSmemBytes = 2 * STAGE * sizeof(__bf16);
+  // Chunks per unrolled loop body: even (LDS buffer parity) and a whole
+  // number of ring turns (ring slots are then compile-time constants).
+  static constexpr int unroll() {
+    int u = 2;
+    while ((u * KS) % P != 0) u += 2;
+    return u;
+  }
+  static constexpr int U = unroll();
   // Two waves per SIMD whenever the accumulators (MR*NT*4 registers) leave
   // room: one wave's epilogue and barriers then overlap the other's MFMAs.
   static constexpr int kWavesPerSimd = MR * NT * 4 <= 128 ? 2 : 1;
   static_assert(N * CPR % THREADS == 0, "staging must divide evenly");
   static_assert((CPR & (CPR - 1)) == 0, "KC/8 must be a power of two");
-  static bool supports(int32_t D) { return D % (KC * AS) == 0; }
-  __device__ __forceinline__ static int row0(int block, int wave) { return (block * NW + wave) * MR * 16; }
+  static bool supports(int32_t D) { return D % (KC * U) == 0; }
+  __device__ __forceinline__ static int row0(int block, int wave) {
+    return (block * WR + wave / WB) * MR * 16;
+  }
+  __device__ __forceinline__ static int col_off(int wave) { return (wave % WB) * NT * 16; }
   __device__ __forceinline__ static bool owns(int /*wave*/, int /*m*/, int /*n*/) { return true; }
 
   // Piece j of staged row n lives at slot j ^ (n mod CPR): the 16 rows a
   // B-fragment read touches at one k land in distinct bank groups.
-  __device__ __forceinline__ static int smem_off(int n, int j) { return n * KC + ((j ^ (n & (CPR - 1))) << 3); }
+  __device__ __forceinline__ static int smem_off(int n, int j) {
+    return n * KC + ((j ^ (n & (CPR - 1))) << 3);
+  }
 
-  __device__ __forceinline__ static void stage_load(const __bf16* __restrict__ h, int32_t B, int32_t D,
-                                    int32_t col0, int c, u32x4 (&reg)[LOADS]) {
+  __device__ __forceinline__ static void stage_load(const __bf16* __restrict__ h, int32_t B,
+                                                    int32_t D, int32_t col0, int c,
+                                                    u32x4 (&reg)[LOADS]) {
     static_for<LOADS>([&](auto i) FS_INLINE {
       const int idx = threadIdx.x + i * THREADS;
       const int n = idx / CPR, j = idx % CPR;
@@ -231,28 +257,32 @@ struct LdsLoop {
     });
   }
 
-  __device__ __forceinline__ static void load_a(const __bf16* const (&arow)[MR], int c, bf16x8 (&a)[KS][MR]) {
-    static_for<KS>([&](auto s) FS_INLINE {
-      static_for<MR>([&](auto m) FS_INLINE { a[s][m] = load_frag<NTL>(arow[m] + c * KC + s * 32); });
-    });
-  }
-
-  __device__ __forceinline__ static void compute(const __bf16* buf, const bf16x8 (&a)[KS][MR],
-                                 f32x4 (&acc)[MR][NT]) {
+  // B fragment of batch tile n at k step s of the chunk in `buf`.
+  __device__ __forceinline__ static bf16x8 bfrag(const __bf16* buf, int s, int n) {
     const int lane = threadIdx.x & (kWave - 1);
     const int li = lane & 15, kb = lane >> 4;
-    static_for<KS>([&](auto s) FS_INLINE {
-      static_for<NT>([&](auto n) FS_INLINE {
-        const bf16x8 bf = __builtin_bit_cast(
-            bf16x8, *reinterpret_cast<const u32x4*>(buf + smem_off(n * 16 + li, s * 4 + kb)));
-        static_for<MR>([&](auto m) FS_INLINE { acc[m][n] = mfma16(a[s][m], bf, acc[m][n]); });
-      });
+    const int c0 = col_off(threadIdx.x >> 6);
+    return __builtin_bit_cast(
+        bf16x8, *reinterpret_cast<const u32x4*>(buf + smem_off(c0 + n * 16 + li, s * 4 + kb)));
+  }
+
+  // One 32-wide k step (s-th of the chunk in `buf`) against all NT batch tiles.
+  __device__ __forceinline__ static void kstep(const __bf16* buf, int s, const bf16x8 (&a)[MR],
+                                               f32x4 (&acc)[MR][NT]) {
+    const int lane = threadIdx.x & (kWave - 1);
+    const int li = lane & 15, kb = lane >> 4;
+    const int c0 = col_off(threadIdx.x >> 6);
+    static_for<NT>([&](auto n) FS_INLINE {
+      const bf16x8 bf = __builtin_bit_cast(
+          bf16x8, *reinterpret_cast<const u32x4*>(buf + smem_off(c0 + n * 16 + li, s * 4 + kb)));
+      static_for<MR>([&](auto m) FS_INLINE { acc[m][n] = mfma16(a[m], bf, acc[m][n]); });
     });
   }
 
-  __device__ __forceinline__ static void run(const __bf16* __restrict__ W, const __bf16* __restrict__ h,
-                             int32_t B, int32_t D, int32_t V, int32_t row0, int32_t col0,
-                             f32x4 (&acc)[MR][NT], void* smem) {
+  __device__ __forceinline__ static void run(const __bf16* __restrict__ W,
+                                             const __bf16* __restrict__ h, int32_t B, int32_t D,
+                                             int32_t V, int32_t row0, int32_t col0,
+                                             f32x4 (&acc)[MR][NT], void* smem) {
     const int lane = threadIdx.x & (kWave - 1);
     const int li = lane & 15, kb = lane >> 4;
     __bf16* hs = static_cast<__bf16*>(smem);
@@ -262,26 +292,61 @@ struct LdsLoop {
     });
     zero_acc(acc);
 
-    // nch is a multiple of AS (see supports), so the unrolled body below has
-    // no branch: every load is issued unconditionally, chunk indices past the
-    // end are clamped (their data is never used), and the in-order vmcnt
-    // accounting lets each chunk wait only for its own operands.
-    const int nch = D / KC;
+    // nch is a multiple of U (see supports), so the unrolled body below has
+    // no branch: every load is issued unconditionally, indices past the end
+    // are clamped (their data is never used), and the in-order vmcnt
+    // accounting lets each k step wait only for its own fragments.
+    const int nch = D / KC, nks = D / 32;
     u32x4 hreg[LOADS];
-    bf16x8 a[AS][KS][MR];
+    bf16x8 ring[P][MR];
     stage_load(h, B, D, col0, 0, hreg);
-    static_for<AS - 1>([&](auto s) FS_INLINE { load_a(arow, min(static_cast<int>(s), nch - 1), a[s]); });
+    static_for<P>([&](auto p) FS_INLINE {
+      const int q = min(static_cast<int>(p), nks - 1);
+      static_for<MR>([&](auto m) FS_INLINE { ring[p][m] = load_frag<NTL>(arow[m] + q * 32); });
+    });
     stage_store(hs, hreg);
     __syncthreads();
 
-    // chunk c uses register slot c % AS and LDS buffer c % 2
-    for (int c0 = 0; c0 < nch; c0 += AS) {
-      static_for<AS>([&](auto s) FS_INLINE {
-        const int c = c0 + s;
+    // chunk c uses LDS buffer c % 2; k step q uses ring slot q % P
+    for (int c0 = 0; c0 < nch; c0 += U) {
+      static_for<U>([&](auto u) FS_INLINE {
+        const int c = c0 + u;
         stage_load(h, B, D, col0, min(c + 1, nch - 1), hreg);
-        load_a(arow, min(c + AS - 1, nch - 1), a[(s + AS - 1) % AS]);
-        compute(hs + (c & 1) * STAGE, a[s], acc);
-        stage_store(hs + ((c + 1) & 1) * STAGE, hreg);  // after the last chunk: unused
+        const __bf16* buf = hs + (u & 1) * STAGE;
+        if constexpr (BR == 0) {
+          static_for<KS>([&](auto s) FS_INLINE {
+            constexpr int slot = (decltype(u)::value * KS + decltype(s)::value) % P;
+            kstep(buf, s, ring[slot], acc);
+            const int q = min(c * KS + s + P, nks - 1);
+            static_for<MR>([&](auto m) FS_INLINE {
+              ring[slot][m] = load_frag<NTL>(arow[m] + q * 32);
+            });
+          });
+        } else {
+          // B fragments of the chunk's (k step, batch tile) sequence are read
+          // BR ahead of their MFMAs; scheduling fences keep the reads early so
+          // LDS latency overlaps MFMA work instead of stalling it.
+          constexpr int T = KS * NT;
+          bf16x8 bq[BR];
+          static_for<BR>([&](auto t) FS_INLINE { bq[t] = bfrag(buf, t / NT, t % NT); });
+          static_for<T>([&](auto tc) FS_INLINE {
+            constexpr int t = decltype(tc)::value, s = t / NT, n = t % NT;
+            constexpr int slot = (decltype(u)::value * KS + s) % P;
+            const bf16x8 cur = bq[t % BR];
+            if constexpr (t + BR < T) bq[t % BR] = bfrag(buf, (t + BR) / NT, (t + BR) % NT);
+            static_for<MR>([&](auto m) FS_INLINE {
+              acc[m][n] = mfma16(ring[slot][m], cur, acc[m][n]);
+            });
+            if constexpr (n == NT - 1) {  // k step s done: refill its W slot
+              const int q = min(c * KS + s + P, nks - 1);
+              static_for<MR>([&](auto m) FS_INLINE {
+                ring[slot][m] = load_frag<NTL>(arow[m] + q * 32);
+              });
+            }
+            __builtin_amdgcn_sched_barrier(0);
+          });
+        }
+        stage_store(hs + ((u + 1) & 1) * STAGE, hreg);  // after the last chunk: unused
         __syncthreads();
       });
     }
