@@ -291,7 +291,8 @@ template <class Loop>
 hipError_t launch_cfg(SampleArgs& a, hipStream_t stream) {
   constexpr int rows = Loop::kRowsPerBlock;
   static_assert(rows >= kMinRowsPerBlock, "split count bound");
-  if (!Loop::supports(a.D)) return hipErrorInvalidValue;
+  if (!Loop::supports(a.D) || static_cast<size_t>(a.B) * a.D * 2 > Loop::kMaxHBytes)
+    return hipErrorInvalidValue;
   constexpr size_t smem = Loop::kSmemBytes;
   if (smem > 0) {  // may exceed the default dynamic-LDS limit: raise it once per kernel
     static const hipError_t attr = [] {
@@ -315,8 +316,8 @@ hipError_t launch_cfg(SampleArgs& a, hipStream_t stream) {
 }
 
 template <class Loop>
-bool supports_cfg(int32_t /*B*/, int32_t D) {
-  return Loop::supports(D);
+bool supports_cfg(int32_t B, int32_t D) {
+  return Loop::supports(D) && static_cast<size_t>(B) * D * 2 <= Loop::kMaxHBytes;
 }
 
 // Blocks of `kernel` that fit on one CU, times the CU count of the current
@@ -385,46 +386,42 @@ constexpr FusedConfig make_persist(const char* name, int order) {
 #define FS_LDS(MR, NT, NW, KC, P, NTL)                                                           \
   make_cfg<LdsLoop<MR, NT, NW, KC, P, NTL>>(                                                   \
       "lds_mr" #MR "_nt" #NT "_nw" #NW "_kc" #KC "_p" #P "_ntl" #NTL, 0)
-#define FS_LDSB(MR, NT, NW, KC, P, WB)                                                         \
-  make_cfg<LdsLoop<MR, NT, NW, KC, P, false, WB>>(                                             \
-      "lds_mr" #MR "_nt" #NT "_nw" #NW "_kc" #KC "_p" #P "_wb" #WB, 0)
 #define FS_LDSR(MR, NT, NW, KC, P, WB, BR)                                                     \
   make_cfg<LdsLoop<MR, NT, NW, KC, P, false, WB, BR>>(                                         \
       "lds_mr" #MR "_nt" #NT "_nw" #NW "_kc" #KC "_p" #P "_wb" #WB "_br" #BR, 0)
+#define FS_DMA(MR, NT, NW, KC, P, S, BR)                                                      \
+  make_cfg<DmaLoop<MR, NT, NW, KC, P, S, BR>>(                                               \
+      "dma_mr" #MR "_nt" #NT "_nw" #NW "_kc" #KC "_p" #P "_s" #S "_br" #BR, 0)
+#define FS_DMAG(MR, NT, NW, KC, P, S, BR, G)                                                  \
+  make_cfg<DmaLoop<MR, NT, NW, KC, P, S, BR, G>>(                                            \
+      "dma_mr" #MR "_nt" #NT "_nw" #NW "_kc" #KC "_p" #P "_s" #S "_br" #BR "_g" #G, 0)
 #define FS_PERSIST(NT, NW, KS, P) \
   make_persist<Persist<NT, NW, KS, P>>("persist_nt" #NT "_nw" #NW "_ks" #KS "_p" #P, 100 + NW)
 
 const FusedConfig kConfigs[] = {
-    FS_KSPLIT(1, 1, 4, 8, 0),        // 0  B <= 8 when no persistent shape fits
-    FS_LDS(2, 4, 4, 64, 8, 0),       // 1  B <= 64
-    FS_LDS(2, 8, 4, 64, 8, 0),       // 2  B <= 128
-    FS_LDS(2, 16, 4, 64, 4, 0),      // 3  B > 128 (batch blocks of 256)
-    FS_STREAM(4, 1, 4, 4, 0),        // 4  any D: fallback for B <= 16
-    FS_STREAM(2, 4, 4, 4, 0),        // 5  any D: fallback for larger B
-    FS_PERSIST(1, 8, 16, 8),         // 6  D = 4096, B <= 16
-    FS_PERSIST(2, 8, 16, 8),         // 7  D = 4096, B <= 32
-    FS_PERSIST(1, 8, 32, 8),         // 8  D = 8192, B <= 16
-    FS_PERSIST(1, 4, 2, 2),          // 9  D = 256 (small shapes)
-    FS_PERSIST(2, 4, 2, 2),          // 10 D = 256
+    FS_KSPLIT(1, 1, 4, 8, 0),           // 0  B <= 8 when no persistent shape fits
+    FS_LDS(2, 4, 4, 64, 4, 0),          // 1  B <= 64 when 14 would leave CUs idle
+    FS_DMAG(4, 8, 8, 64, 4, 3, 4, 2),   // 2  B <= 128
+    FS_DMAG(2, 16, 8, 64, 4, 4, 4, 2),  // 3  B > 128 (batch blocks of 256)
+    FS_STREAM(4, 1, 4, 4, 0),           // 4  any D: fallback for B <= 16
+    FS_STREAM(2, 4, 4, 4, 0),           // 5  any D: fallback for larger B
+    FS_PERSIST(1, 8, 16, 8),            // 6  D = 4096, B <= 16
+    FS_PERSIST(2, 8, 16, 8),            // 7  D = 4096, B <= 32
+    FS_PERSIST(1, 8, 32, 8),            // 8  D = 8192, B <= 16
+    FS_PERSIST(1, 4, 2, 2),             // 9  D = 256 (small shapes)
+    FS_PERSIST(2, 4, 2, 2),             // 10 D = 256
+    FS_LDS(2, 16, 4, 64, 4, 0),         // 11 B > 128 when 2*B*D >= 2^31
+    FS_LDSR(2, 16, 4, 64, 4, 1, 4),     // 12 B > 128 when 3 would leave CUs idle
+    FS_LDSR(4, 8, 4, 64, 4, 1, 4),      // 13 B <= 128 when 2 would leave CUs idle
+    FS_DMAG(4, 4, 8, 64, 4, 3, 4, 2),   // 14 B <= 64
     // alternatives for tuning sweeps
     FS_PERSIST(1, 8, 16, 16),
-    FS_LDS(2, 4, 4, 64, 4, 0),
-    FS_LDS(4, 4, 4, 64, 4, 0),
-    FS_LDS(4, 4, 4, 64, 8, 0),
-    FS_LDS(2, 8, 4, 64, 4, 0),
-    FS_LDS(4, 8, 4, 64, 4, 0),
-    FS_LDS(2, 16, 4, 64, 2, 0),
-    FS_LDS(2, 16, 8, 64, 4, 0),
-    FS_LDSB(4, 8, 8, 64, 4, 2),
-    FS_LDSR(2, 16, 4, 64, 2, 1, 4),
-    FS_LDSR(2, 16, 4, 64, 2, 1, 6),
-    FS_LDSR(2, 16, 4, 64, 4, 1, 4),
-    FS_LDSR(4, 8, 4, 64, 4, 1, 4),
+    FS_LDS(2, 8, 4, 64, 8, 0),
     FS_LDSR(2, 8, 4, 64, 8, 1, 4),
-    FS_LDSR(2, 4, 4, 64, 8, 1, 4),
-    FS_LDSR(4, 8, 8, 64, 4, 2, 4),
-    FS_LDSR(4, 16, 4, 64, 4, 1, 4),
-    FS_LDSR(4, 16, 4, 64, 2, 1, 4),
+    FS_DMA(2, 16, 8, 64, 4, 4, 4),
+    FS_DMA(4, 8, 8, 64, 4, 3, 4),
+    FS_DMAG(2, 16, 8, 64, 8, 3, 4, 2),
+    FS_DMAG(2, 8, 8, 64, 4, 4, 4, 2),
     FS_KSPLIT(2, 1, 4, 8, 0),
     FS_KSPLIT(4, 2, 4, 4, 0),
     FS_STREAM(1, 1, 4, 8, 0),
@@ -433,8 +430,9 @@ const FusedConfig kConfigs[] = {
 #undef FS_KSPLIT
 #undef FS_LDS
 #undef FS_PERSIST
-#undef FS_LDSB
 #undef FS_LDSR
+#undef FS_DMA
+#undef FS_DMAG
 
 constexpr int kNumConfigs = sizeof(kConfigs) / sizeof(kConfigs[0]);
 
@@ -458,16 +456,47 @@ bool fused_config_supports(int id, int32_t B, int32_t D) {
   return id >= 0 && id < kNumConfigs && kConfigs[id].supports(B, D);
 }
 
-int fused_auto_config(int32_t B, int32_t D, int32_t /*V*/) {
-  // persistent K-split where h fits in registers, else by batch size
+namespace {
+int device_cus() {
+  static int cached_dev = -1, cached = 0;
+  int dev = 0;
+  if (hipGetDevice(&dev) != hipSuccess) return 0;
+  if (dev != cached_dev) {
+    int cus = 0;
+    if (hipDeviceGetAttribute(&cus, hipDeviceAttributeMultiprocessorCount, dev) != hipSuccess)
+      return 0;
+    cached = cus;
+    cached_dev = dev;
+  }
+  return cached;
+}
+
+// Share of CU slots busy over the whole grid of a configuration that runs one
+// block per CU: blocks / (rounds * CUs).  A grid whose last round is mostly
+// empty wastes that round.
+double one_per_cu_fill(int id, int32_t V) {
+  const int cus = device_cus();
+  if (cus <= 0) return 0.0;
+  const int rows = kConfigs[id].rows_per_block;
+  const long blocks = (static_cast<long>(V) + rows - 1) / rows;
+  const long rounds = (blocks + cus - 1) / cus;
+  return static_cast<double>(blocks) / (static_cast<double>(rounds) * cus);
+}
+}  // namespace
+
+int fused_auto_config(int32_t B, int32_t D, int32_t V) {
+  // persistent K-split where h fits in registers
   for (int id : {6, 7, 8})
     if (kConfigs[id].supports(B, D)) return id;
-  int id;
-  if (B <= 8) id = 0;
-  else if (B <= 64) id = 1;
-  else if (B <= 128) id = 2;
-  else id = 3;
-  if (kConfigs[id].supports(B, D)) return id;
+  if (B <= 8 && kConfigs[0].supports(B, D)) return 0;
+  // batch-tiled loops: the DMA-staged loop (one 8-wave block per CU) when its
+  // grid fills the CUs, else the LDS loop (smaller blocks, two per CU)
+  struct Pick { int dma, lds; };
+  const Pick p = B <= 64 ? Pick{14, 1} : (B <= 128 ? Pick{2, 13} : Pick{3, 12});
+  constexpr double kMinFill = 0.85;
+  if (kConfigs[p.dma].supports(B, D) && one_per_cu_fill(p.dma, V) >= kMinFill) return p.dma;
+  if (kConfigs[p.lds].supports(B, D)) return p.lds;
+  if (B > 64 && kConfigs[11].supports(B, D)) return 11;
   return B <= 16 ? 4 : 5;
 }
 

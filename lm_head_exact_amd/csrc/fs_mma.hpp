@@ -26,6 +26,9 @@
 //   LdsLoop     each wave owns MR*16 rows; h is staged through LDS in
 //               KC-wide chunks (double-buffered, XOR-swizzled 16-byte pieces)
 //               and shared by the block's waves (large batches).
+//   DmaLoop     as LdsLoop, but h reaches LDS by direct buffer->LDS loads in
+//               an S-deep ring, with explicit load-count waits so that the W
+//               stream keeps its lead across chunk barriers (large batches).
 // Rows >= V and batch rows >= B read clamped (valid) addresses; their results
 // are discarded by the epilogue, so operands need no masking except for the
 // k >= D tail of the stream loop.  W loads may use the non-temporal hint (NTL):
@@ -124,6 +127,7 @@ struct StreamLoop {
   static constexpr size_t kSmemBytes = 0;
   static constexpr int kWavesPerSimd = 1;  // occupancy hint: none
   static bool supports(int32_t /*D*/) { return true; }
+  static constexpr size_t kMaxHBytes = ~size_t{0};
   static constexpr int kBlockCols = NT * 16;
   __device__ __forceinline__ static int row0(int block, int wave) { return (block * NW + wave) * MR * 16; }
   __device__ __forceinline__ static int col_off(int /*wave*/) { return 0; }
@@ -157,6 +161,7 @@ struct KSplitLoop {
   static constexpr size_t kSmemBytes = static_cast<size_t>(NW) * MR * NT * kWave * sizeof(f32x4);
   static constexpr int kWavesPerSimd = 1;
   static bool supports(int32_t D) { return D % (32 * NW) == 0; }
+  static constexpr size_t kMaxHBytes = ~size_t{0};
   static constexpr int kBlockCols = NT * 16;
   __device__ __forceinline__ static int row0(int block, int /*wave*/) { return block * MR * 16; }
   __device__ __forceinline__ static int col_off(int /*wave*/) { return 0; }
@@ -226,6 +231,7 @@ struct LdsLoop {
   static_assert(N * CPR % THREADS == 0, "staging must divide evenly");
   static_assert((CPR & (CPR - 1)) == 0, "KC/8 must be a power of two");
   static bool supports(int32_t D) { return D % (KC * U) == 0; }
+  static constexpr size_t kMaxHBytes = ~size_t{0};
   __device__ __forceinline__ static int row0(int block, int wave) {
     return (block * WR + wave / WB) * MR * 16;
   }
@@ -350,6 +356,175 @@ struct LdsLoop {
         __syncthreads();
       });
     }
+  }
+};
+
+// ---------------------------------------------------------------------------
+// DmaLoop: every wave of the block owns MR*16 distinct vocabulary rows and
+// shares one batch tile of NT*16 rows.  h is staged into LDS by direct
+// global->LDS loads (no register round trip, no LDS store instructions) in a
+// ring of S KC-wide chunks issued S-1 chunks ahead; W fragments stream into a
+// ring of P k-steps held in registers.  Loads complete in issue order, so each
+// chunk's wait names the exact number of younger loads it may leave in flight:
+// the W stream keeps its P-step lead across chunk boundaries.
+// Requires D % (KC * U) == 0.
+// ---------------------------------------------------------------------------
+template <int MR_, int NT_, int NW_, int KC, int P, int S, int BR, int G = 1>
+struct DmaLoop {
+  static constexpr int MR = MR_, NT = NT_, NW = NW_;
+  static constexpr int kRowsPerBlock = MR * 16 * NW;
+  static constexpr int kBlockCols = NT * 16;
+  static constexpr int KS = KC / 32;                 // MFMA k-steps per chunk
+  static constexpr int CPR = KC / 8;                 // 16-byte pieces per staged row
+  static constexpr int STAGE = kBlockCols * KC;      // bf16 elements per ring slot
+  static constexpr int IPW = kBlockCols * CPR / (NW * kWave);  // direct loads per wave per chunk
+  static_assert(kBlockCols * CPR % (NW * kWave) == 0, "staging must divide evenly");
+  static_assert((CPR & (CPR - 1)) == 0, "KC/8 must be a power of two");
+  static_assert(S >= 2 && BR >= 1 && BR <= KS * NT, "ring shapes");
+  static constexpr size_t kSmemBytes = static_cast<size_t>(S) * STAGE * sizeof(__bf16);
+  static constexpr int kWavesPerSimd = (NW + 3) / 4;
+  // W slots are refilled in bursts of G consecutive k-steps, so that the
+  // 64*G bytes a row contributes to one burst reach the memory controller
+  // together and share DRAM page openings.
+  static_assert(P % G == 0 && P >= G, "the W ring is refilled in whole bursts");
+  // chunks per unrolled body: a whole number of W ring turns
+  static constexpr int unroll() {
+    int u = 1;
+    while ((u * KS) % P != 0) ++u;
+    return u;
+  }
+  static constexpr int U = unroll();
+  // A lower bound on the loads a wave issues after chunk c+1's staging loads
+  // and before the end of chunk c: S-2 younger staging groups plus the W
+  // bursts completed in the S-1 chunks between (the ring prefill, P k-steps,
+  // stands in for them in the first chunks).
+  static constexpr int kWindowW = G * (((S - 1) * KS) / G);
+  static constexpr int kYounger = (S - 2) * IPW + MR * (P < kWindowW ? P : kWindowW);
+  static_assert(kYounger <= 63, "vmcnt holds at most 63");
+  static bool supports(int32_t D) { return D % (KC * U) == 0; }
+  static constexpr size_t kMaxHBytes = 0x7FFFFFFF;  // buffer offsets are 32-bit
+  // raw buffer resource word 3 for gfx9-family parts (untyped 32-bit data)
+  static constexpr int kBufferFlags = 0x00020000;
+  __device__ __forceinline__ static int row0(int block, int wave) { return (block * NW + wave) * MR * 16; }
+  __device__ __forceinline__ static int col_off(int /*wave*/) { return 0; }
+  __device__ __forceinline__ static bool owns(int /*wave*/, int /*m*/, int /*n*/) { return true; }
+
+  // Piece j of staged row n lives at slot j ^ (n mod CPR).
+  __device__ __forceinline__ static int smem_off(int n, int j) {
+    return n * KC + ((j ^ (n & (CPR - 1))) << 3);
+  }
+
+  // Chunk c of the block's h rows into ring slot `buf`.  Load i of wave w
+  // fills the 64 consecutive 16-byte slots starting at (w*IPW + i)*64, lane
+  // l the slot p = that + l: staged row n = p / CPR holding k-piece
+  // (p % CPR) ^ (n % CPR), the inverse of smem_off's swizzle.  The loads are
+  // buffer loads (32-bit byte offsets into h, so 2*B*D < 2^31): unlike the
+  // global form they are not counted as possible LDS accesses of unknown
+  // order, which would force every B-fragment read to drain the LDS queue.
+  __device__ __forceinline__ static void stage(const __bf16* __restrict__ h, int32_t B, int32_t D,
+                                               int32_t col0, int c, __bf16* buf) {
+    const int lane = threadIdx.x & (kWave - 1), wave = threadIdx.x >> 6;
+    const __amdgpu_buffer_rsrc_t rsrc = __builtin_amdgcn_make_buffer_rsrc(
+        const_cast<__bf16*>(h), 0, B * D * 2, kBufferFlags);
+    static_for<IPW>([&](auto i) FS_INLINE {
+      const int base = (wave * IPW + i) * kWave;
+      const int p = base + lane;
+      const int n = p / CPR, j = (p % CPR) ^ (n & (CPR - 1));
+      const int b = min(col0 + n, B - 1);
+      __builtin_amdgcn_raw_ptr_buffer_load_lds(rsrc, buf + base * 8, 16,
+                                               (b * D + c * KC + j * 8) * 2, 0, 0, 0);
+    });
+  }
+
+  // s_waitcnt with only the vector-memory counter constrained (gfx9 encoding).
+  template <int N>
+  __device__ __forceinline__ static void wait_vm() {
+    static_assert(N >= 0 && N <= 63, "vmcnt range");
+    __builtin_amdgcn_s_waitcnt((N & 0xF) | ((N >> 4) << 14) | (0x7 << 4) | (0xF << 8));
+  }
+
+  // Workgroup barrier without the release fence of __syncthreads: that fence
+  // would wait for every outstanding load, W fragments included, because
+  // staging loads write LDS.  Each wave has already waited for its own staging
+  // loads of the next chunk (wait_vm), and every B-fragment read of the
+  // current chunk has been consumed by an MFMA, so LDS is consistent here;
+  // the empty asm with a memory clobber and the scheduling fences keep the
+  // compiler from moving LDS accesses across the barrier.
+  __device__ __forceinline__ static void barrier() {
+    __builtin_amdgcn_sched_barrier(0);
+    asm volatile("" ::: "memory");
+    __builtin_amdgcn_s_barrier();
+    asm volatile("" ::: "memory");
+    __builtin_amdgcn_sched_barrier(0);
+  }
+
+  __device__ __forceinline__ static bf16x8 bfrag(const __bf16* buf, int s, int n) {
+    const int lane = threadIdx.x & (kWave - 1);
+    const int li = lane & 15, kb = lane >> 4;
+    return __builtin_bit_cast(
+        bf16x8, *reinterpret_cast<const u32x4*>(buf + smem_off(n * 16 + li, s * 4 + kb)));
+  }
+
+  __device__ __forceinline__ static void run(const __bf16* __restrict__ W,
+                                             const __bf16* __restrict__ h, int32_t B, int32_t D,
+                                             int32_t V, int32_t row0, int32_t col0,
+                                             f32x4 (&acc)[MR][NT], void* smem) {
+    const int lane = threadIdx.x & (kWave - 1);
+    const int li = lane & 15, kb = lane >> 4;
+    __bf16* hs = static_cast<__bf16*>(smem);
+    const __bf16* arow[MR];
+    static_for<MR>([&](auto m) FS_INLINE {
+      arow[m] = W + static_cast<size_t>(min(row0 + m * 16 + li, V - 1)) * D + 8 * kb;
+    });
+    zero_acc(acc);
+
+    // Every load is issued unconditionally (indices past the end are clamped
+    // and their data never used), so the per-chunk load counts are constants.
+    const int nch = D / KC, nks = D / 32;
+    static_for<S - 1>([&](auto s) FS_INLINE { stage(h, B, D, col0, min(static_cast<int>(s), nch - 1), hs + s * STAGE); });
+    bf16x8 ring[P][MR];
+    static_for<P>([&](auto p) FS_INLINE {
+      const int q = min(static_cast<int>(p), nks - 1);
+      static_for<MR>([&](auto m) FS_INLINE { ring[p][m] = load_frag(arow[m] + q * 32); });
+    });
+    wait_vm<(S - 2) * IPW + P * MR>();  // chunk 0 staged
+    barrier();
+
+    int slot_c = 0;  // ring slot of chunk c
+    for (int c0 = 0; c0 < nch; c0 += U) {
+      static_for<U>([&](auto u) FS_INLINE {
+        const int c = c0 + u;
+        const int slot_n = slot_c == 0 ? S - 1 : slot_c - 1;  // slot of chunk c + S - 1
+        stage(h, B, D, col0, min(c + S - 1, nch - 1), hs + slot_n * STAGE);
+        __builtin_amdgcn_sched_barrier(0);
+        const __bf16* buf = hs + slot_c * STAGE;
+        constexpr int T = KS * NT;
+        bf16x8 bq[BR];
+        static_for<BR>([&](auto t) FS_INLINE { bq[t] = bfrag(buf, t / NT, t % NT); });
+        static_for<T>([&](auto tc) FS_INLINE {
+          constexpr int t = decltype(tc)::value, s = t / NT, n = t % NT;
+          constexpr int slot = (decltype(u)::value * KS + s) % P;
+          const bf16x8 cur = bq[t % BR];
+          if constexpr (t + BR < T) bq[t % BR] = bfrag(buf, (t + BR) / NT, (t + BR) % NT);
+          static_for<MR>([&](auto m) FS_INLINE { acc[m][n] = mfma16(ring[slot][m], cur, acc[m][n]); });
+          // k-step g = c*KS + s done; at the end of each G-step burst refill
+          // the burst's slots with the k-steps P ahead
+          constexpr int g = decltype(u)::value * KS + s;  // g mod (U*KS)
+          if constexpr (n == NT - 1 && (g + 1) % G == 0) {
+            static_for<G>([&](auto j) FS_INLINE {
+              constexpr int sl = (g + 1 - G + decltype(j)::value) % P;
+              const int q = min(c * KS + s + 1 - G + decltype(j)::value + P, nks - 1);
+              static_for<MR>([&](auto m) FS_INLINE { ring[sl][m] = load_frag(arow[m] + q * 32); });
+            });
+          }
+          __builtin_amdgcn_sched_barrier(0);
+        });
+        wait_vm<kYounger>();  // chunk c + 1 staged (this wave's share)
+        barrier();            // ... and every wave's; slot c is free again
+        slot_c = slot_c == S - 1 ? 0 : slot_c + 1;
+      });
+    }
+    wait_vm<0>();  // the trailing (clamped) staging loads land before LDS is reused
   }
 };
 
