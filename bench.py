@@ -59,15 +59,15 @@ TRAFFIC_PROFILE = os.path.join(ROOT, "profiles", "fused_sample_llama3_b32_hbm_tr
 
 
 def kernel_sources_sha256():
-    """Fingerprint of the HIP sources: counters taken on other sources no
-    longer describe the kernel that runs."""
+    """Fingerprint of the sources the fused sampler kernels are compiled
+    from: counters taken on other sources no longer describe the kernel that
+    runs.  (The unfused baseline and the host-side API live in other files.)"""
     import hashlib
     csrc = os.path.join(ROOT, "lm_head_exact_amd", "csrc")
     h = hashlib.sha256()
-    for name in sorted(os.listdir(csrc)):
-        if name.endswith((".hip", ".hpp")):
-            h.update(name.encode())
-            h.update(open(os.path.join(csrc, name), "rb").read())
+    for name in ("fs_device.hpp", "fs_internal.hpp", "fs_mma.hpp", "fs_fused.hip"):
+        h.update(name.encode())
+        h.update(open(os.path.join(csrc, name), "rb").read())
     return h.hexdigest()
 
 

@@ -55,33 +55,56 @@ UnfusedLayout layout(int32_t B, int32_t V, void* ws) {
   return L;
 }
 
-template <int MR, int NT, int NW>
-__global__ __launch_bounds__(NW * kWave) void gemm_logits_kernel(SampleArgs a, float* z,
-                                                                 int64_t ldz) {
+// logits z[b][v] for a (Loop::kRowsPerBlock x Loop::kBlockCols) tile per
+// block, with the same main loops as the fused sampler.
+template <class Loop>
+__global__ __launch_bounds__(Loop::NW * kWave)
+__attribute__((amdgpu_waves_per_eu(Loop::kWavesPerSimd))) void gemm_logits_kernel(SampleArgs a,
+                                                                                  float* z,
+                                                                                  int64_t ldz) {
+  constexpr int MR = Loop::MR, NT = Loop::NT;
+  extern __shared__ __attribute__((aligned(16))) unsigned char dyn_smem[];
   const int lane = threadIdx.x & (kWave - 1);
   const int wave = threadIdx.x >> 6;
   const int li = lane & 15, kb = lane >> 4;
-  const int row0 = (blockIdx.x * NW + wave) * (MR * 16);
-  const int col0 = blockIdx.y * (NT * 16);
+  const int row0 = Loop::row0(blockIdx.x, wave);
+  const int block_col0 = blockIdx.y * Loop::kBlockCols;
   f32x4 acc[MR][NT];
-  StreamLoop<MR, NT, NW, 4, false>::run(a.W, a.h, a.B, a.D, a.V, row0, col0, acc, nullptr);
-#pragma unroll
-  for (int n = 0; n < NT; ++n) {
+  Loop::run(a.W, a.h, a.B, a.D, a.V, row0, block_col0, acc, dyn_smem);
+  const int col0 = block_col0 + Loop::col_off(wave);
+  static_for<NT>([&](auto n) FS_INLINE {
     const int b = col0 + n * 16 + li;
-    if (b >= a.B) continue;
-#pragma unroll
-    for (int m = 0; m < MR; ++m) {
-      const int v0 = row0 + m * 16 + 4 * kb;
-      float* dst = z + b * ldz + v0;
-      if (v0 + 3 < a.V) {
-        *reinterpret_cast<f32x4*>(dst) = acc[m][n];  // ldz % 4 == 0, v0 % 4 == 0
-      } else {
-#pragma unroll
-        for (int r = 0; r < 4; ++r)
-          if (v0 + r < a.V) dst[r] = acc[m][n][r];
-      }
+    if (b < a.B) {
+      static_for<MR>([&](auto m) FS_INLINE {
+        if (Loop::owns(wave, m, n)) {
+          const int v0 = row0 + m * 16 + 4 * kb;
+          float* dst = z + b * ldz + v0;
+          if (v0 + 3 < a.V) {
+            *reinterpret_cast<f32x4*>(dst) = acc[m][n];  // ldz % 4 == 0, v0 % 4 == 0
+          } else {
+            static_for<4>([&](auto r) FS_INLINE {
+              if (v0 + r < a.V) dst[r] = acc[m][n][decltype(r)::value];
+            });
+          }
+        }
+      });
     }
+  });
+}
+
+template <class Loop>
+hipError_t launch_gemm(const SampleArgs& a, float* z, int64_t ldz, hipStream_t stream) {
+  constexpr size_t smem = Loop::kSmemBytes;
+  if (smem > 0) {
+    static const hipError_t attr = hipFuncSetAttribute(
+        reinterpret_cast<const void*>(&gemm_logits_kernel<Loop>),
+        hipFuncAttributeMaxDynamicSharedMemorySize, static_cast<int>(smem));
+    if (attr != hipSuccess) return attr;
   }
+  const dim3 grid((a.V + Loop::kRowsPerBlock - 1) / Loop::kRowsPerBlock,
+                  (a.B + Loop::kBlockCols - 1) / Loop::kBlockCols);
+  gemm_logits_kernel<Loop><<<grid, Loop::NW * kWave, smem, stream>>>(a, z, ldz);
+  return hipGetLastError();
 }
 
 // Block-wide reductions over kThreads threads.
@@ -215,10 +238,12 @@ hipError_t launch_unfused(const SampleArgs& a, int32_t* out_ids, float* out_val,
                           void* workspace, hipStream_t stream) {
   const UnfusedLayout L = layout(a.B, a.V, workspace);
   {
-    constexpr int MR = 2, NT = 2, NW = 4;
-    const dim3 grid((a.V + MR * 16 * NW - 1) / (MR * 16 * NW), (a.B + NT * 16 - 1) / (NT * 16));
-    gemm_logits_kernel<MR, NT, NW><<<grid, NW * kWave, 0, stream>>>(a, L.logits, L.ldz);
-    hipError_t e = hipGetLastError();
+    // the contraction with the fused sampler's main loops: W read once per
+    // batch block of 32 (streamed) or 256 (h staged in LDS) rows
+    using Big = LdsLoop<2, 16, 4, 64, 4, false, 1, 4>;
+    const hipError_t e = a.B > 32 && Big::supports(a.D)
+                             ? launch_gemm<Big>(a, L.logits, L.ldz, stream)
+                             : launch_gemm<StreamLoop<2, 2, 4, 4, false>>(a, L.logits, L.ldz, stream);
     if (e != hipSuccess) return e;
   }
   const dim3 rows(L.C, a.B);
