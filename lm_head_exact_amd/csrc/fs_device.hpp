@@ -58,7 +58,10 @@ struct Philox {
       const uint64_t q = static_cast<uint64_t>(0xCD9E8D57u) * c.z;
       const uint32_t p_hi = static_cast<uint32_t>(p >> 32), p_lo = static_cast<uint32_t>(p);
       const uint32_t q_hi = static_cast<uint32_t>(q >> 32), q_lo = static_cast<uint32_t>(q);
-      c = u32x4{q_hi ^ c.y ^ a, q_lo, p_hi ^ c.w ^ b, p_lo};
+      // three-input xors as single v_bitop3_b32 (truth table 0x96 = a ^ b ^ c)
+      const uint32_t c0 = static_cast<uint32_t>(__builtin_amdgcn_bitop3_b32(q_hi, c.y, a, 0x96));
+      const uint32_t c2 = static_cast<uint32_t>(__builtin_amdgcn_bitop3_b32(p_hi, c.w, b, 0x96));
+      c = u32x4{c0, q_lo, c2, p_lo};
       a += 0x9E3779B9u;
       b += 0xBB67AE85u;
     }
@@ -93,18 +96,18 @@ __device__ __forceinline__ uint32_t pick_word(u32x4 w, uint32_t i) {
 // on all 2^23 grid points.
 __device__ __forceinline__ float gumbel_from_bits(uint32_t x) {
   constexpr float kLn2 = 0.693147180559945309f;
-  const uint32_t k = x >> 9;
-  const float u = static_cast<float>(2u * k + 1u) * 0x1p-24f;
-  const float v = static_cast<float>(0xFFFFFFu - 2u * k) * 0x1p-24f;
-  float series = 1.0f / 7.0f;
-  series = __builtin_fmaf(series, v, 1.0f / 6.0f);
-  series = __builtin_fmaf(series, v, 1.0f / 5.0f);
+  const float u = static_cast<float>(2u * (x >> 9) + 1u) * 0x1p-24f;  // exact
+  // v = 1 - u is exact for u >= 1/2 (Sterbenz), so wherever the series below
+  // is used; the series stops at v^5/5, a relative truncation error below
+  // v^5/6 <= 1.6e-7 for v <= 1/16.
+  const float v = 1.0f - u;
+  float series = 1.0f / 5.0f;
   series = __builtin_fmaf(series, v, 1.0f / 4.0f);
   series = __builtin_fmaf(series, v, 1.0f / 3.0f);
   series = __builtin_fmaf(series, v, 1.0f / 2.0f);
   series = __builtin_fmaf(series, v, 1.0f);
   series *= v;
-  const float neg_ln_u = v <= 0.0625f ? series : -__builtin_amdgcn_logf(u) * kLn2;
+  const float neg_ln_u = u >= 0.9375f ? series : -__builtin_amdgcn_logf(u) * kLn2;
   return -__builtin_amdgcn_logf(neg_ln_u) * kLn2;
 }
 
@@ -155,6 +158,35 @@ __device__ __forceinline__ float row_inv_temperature(float T) {
 // separately rounded operations (no contraction into a fused multiply-add).
 __device__ __forceinline__ float perturbed_score(float z, float inv_t, float g) {
   return __fadd_rn(__fmul_rn(z, inv_t), g);
+}
+
+// Pushes the scores of four consecutive logits z (local vocabulary rows
+// v0 .. v0+3, global ids gv0 .. gv0+3, batch row `row`) into `best`.  Rows
+// at or past V score -inf and never win; greedy rows score the logit itself.
+// Everything is computed on every lane and selected, without branches: the
+// lanes of a wave hold different batch rows, so a branch would serialise.
+// ALIGN4: gv0 % 4 == 0, so the four ids share one Philox block.
+template <bool ALIGN4>
+__device__ __forceinline__ void push_four(ArgMax& best, f32x4 z, int v0, int32_t V, uint32_t gv0,
+                                          uint32_t row, uint64_t step, bool greedy,
+                                          float inv_t, const Philox& philox) {
+  const u32x4 w0 = philox(noise_counter(gv0, row, step));
+  u32x4 w1 = w0;
+  if (!ALIGN4) w1 = philox(noise_counter(gv0 + 4u, row, step));
+  static_for<4>([&](auto rc) FS_INLINE {
+    constexpr int r = decltype(rc)::value;
+    uint32_t x;
+    if (ALIGN4) {
+      x = w0[r];
+    } else {
+      const uint32_t q = (gv0 & 3u) + r;  // word index across the two blocks
+      x = q < 4u ? pick_word(w0, q) : pick_word(w1, q - 4u);
+    }
+    const float noisy = perturbed_score(z[r], inv_t, gumbel_from_bits(x));
+    float s = greedy ? z[r] : noisy;
+    s = v0 + r < V ? s : -__builtin_inff();
+    best.push_ascending(s, static_cast<int32_t>(gv0 + r));
+  });
 }
 
 }  // namespace fs

@@ -28,9 +28,22 @@ __attribute__((amdgpu_waves_per_eu(Loop::kWavesPerSimd))) void fused_sample_kern
   const int row0 = Loop::row0(blockIdx.x, wave);
   const int block_col0 = blockIdx.y * Loop::kBlockCols;
 
+  const int col0 = block_col0 + Loop::col_off(wave);  // this wave's first batch row
+  // The temperatures of the wave's batch rows are loaded all at once, before
+  // the main loop where the loop leaves registers for them, else right after
+  // it: loaded next to their uses, each batch tile would wait one full memory
+  // latency of a busy HBM.
+  float temp[NT];
+  auto load_temperatures = [&]() FS_INLINE {
+    static_for<NT>([&](auto n) FS_INLINE {
+      temp[n] = a.temperature[min(col0 + static_cast<int>(n) * 16 + li, a.B - 1)];
+    });
+  };
+  if constexpr (Loop::kEarlyTemperature) load_temperatures();
+
   f32x4 acc[MR][NT];
   Loop::run(a.W, a.h, a.B, a.D, a.V, row0, block_col0, acc, dyn_smem);
-  const int col0 = block_col0 + Loop::col_off(wave);  // this wave's first batch row
+  if constexpr (!Loop::kEarlyTemperature) load_temperatures();
 
   // ---- epilogue: scale, perturb, running (max, argmax) per batch row ----
   // Lane (li, kb) holds batch row col0 + 16n + li and vocabulary rows
@@ -39,43 +52,18 @@ __attribute__((amdgpu_waves_per_eu(Loop::kWavesPerSimd))) void fused_sample_kern
   ArgMax best[NT];
   static_for<NT>([&](auto n) FS_INLINE {
     best[n].init();
+    // rows b >= B run on a clamped temperature; their results are not written
     const int b = col0 + n * 16 + li;
-    if (b < a.B) {
-      const float T = a.temperature[b];
-      const bool greedy = row_is_greedy(T);
-      const float inv_t = row_inv_temperature(T);
-      static_for<MR>([&](auto m) FS_INLINE {
-        if (Loop::owns(wave, m, n)) {
-          const int v0 = row0 + m * 16 + 4 * kb;  // a multiple of 4
-          const uint32_t gv0 = static_cast<uint32_t>(a.vocab_offset + v0);
-          // ids gv0 .. gv0+3 lie in Philox blocks gv0/4 and (when vocab_offset
-          // is not a multiple of 4) gv0/4 + 1
-          u32x4 w0 = u32x4{0u, 0u, 0u, 0u}, w1 = w0;
-          if (!greedy) {
-            w0 = philox(noise_counter(gv0, b, a.step));
-            if (!ALIGN4) w1 = philox(noise_counter(gv0 + 4u, b, a.step));
-          }
-          static_for<4>([&](auto rc) FS_INLINE {
-            constexpr int r = decltype(rc)::value;
-            if (v0 + r < a.V) {
-              const uint32_t gv = gv0 + r;
-              float s = acc[m][n][r];
-              if (!greedy) {
-                uint32_t x;
-                if (ALIGN4) {
-                  x = w0[r];
-                } else {
-                  const uint32_t q = (gv0 & 3u) + r;  // word index across the two blocks
-                  x = q < 4u ? pick_word(w0, q) : pick_word(w1, q - 4u);
-                }
-                s = perturbed_score(s, inv_t, gumbel_from_bits(x));
-              }
-              best[n].push_ascending(s, static_cast<int32_t>(gv));  // gv grows with (m, r)
-            }
-          });
-        }
-      });
-    }
+    const float T = temp[n];
+    const bool greedy = row_is_greedy(T);
+    const float inv_t = row_inv_temperature(T);
+    static_for<MR>([&](auto m) FS_INLINE {
+      if (Loop::owns(wave, m, n)) {
+        const int v0 = row0 + m * 16 + 4 * kb;  // a multiple of 4
+        push_four<ALIGN4>(best[n], acc[m][n], v0, a.V, static_cast<uint32_t>(a.vocab_offset + v0),
+                          static_cast<uint32_t>(b), a.step, greedy, inv_t, philox);
+      }
+    });
   });
   // lanes l, l^16, l^32, l^48 hold the same batch row
   static_for<NT>([&](auto n) FS_INLINE {
@@ -188,30 +176,9 @@ __global__ __launch_bounds__(NW * kWave) void persist_sample_kernel(SampleArgs a
         f32x4 z = red[((par * NW + 0) * NT + n) * kWave + lane];
         for (int w = 1; w < NW; ++w) z += red[((par * NW + w) * NT + n) * kWave + lane];
         const int b = n * 16 + li;
-        const int v0 = g * 16 + 4 * kb;
-        const uint32_t gv0 = static_cast<uint32_t>(a.vocab_offset + v0);
-        u32x4 w0 = u32x4{0u, 0u, 0u, 0u}, w1 = w0;
-        if (!greedy[n]) {
-          w0 = philox(noise_counter(gv0, b, a.step));
-          if (!ALIGN4) w1 = philox(noise_counter(gv0 + 4u, b, a.step));
-        }
-        static_for<4>([&](auto rc) FS_INLINE {
-          constexpr int r = decltype(rc)::value;
-          if (v0 + r < a.V) {
-            float sc = z[r];
-            if (!greedy[n]) {
-              uint32_t x;
-              if (ALIGN4) {
-                x = w0[r];
-              } else {
-                const uint32_t q = (gv0 & 3u) + r;
-                x = q < 4u ? pick_word(w0, q) : pick_word(w1, q - 4u);
-              }
-              sc = perturbed_score(sc, inv_t[n], gumbel_from_bits(x));
-            }
-            best[n].push_ascending(sc, static_cast<int32_t>(gv0 + r));  // g grows per owner
-          }
-        });
+        const int v0 = g * 16 + 4 * kb;  // ids grow with g for each owner
+        push_four<ALIGN4>(best[n], z, v0, a.V, static_cast<uint32_t>(a.vocab_offset + v0),
+                          static_cast<uint32_t>(b), a.step, greedy[n], inv_t[n], philox);
       }
     });
   }

@@ -123,6 +123,8 @@ __device__ __forceinline__ void pipelined_ksteps(const FragPtrs<MR, NT>& ptr, in
 template <int MR_, int NT_, int NW_, int P, bool NTL>
 struct StreamLoop {
   static constexpr int MR = MR_, NT = NT_, NW = NW_;
+  // the epilogue's per-row temperatures are loaded after the main loop
+  static constexpr bool kEarlyTemperature = false;
   static constexpr int kRowsPerBlock = MR * 16 * NW;
   static constexpr size_t kSmemBytes = 0;
   static constexpr int kWavesPerSimd = 1;  // occupancy hint: none
@@ -157,6 +159,8 @@ struct StreamLoop {
 template <int MR_, int NT_, int NW_, int P, bool NTL>
 struct KSplitLoop {
   static constexpr int MR = MR_, NT = NT_, NW = NW_;
+  // the epilogue's per-row temperatures are loaded after the main loop
+  static constexpr bool kEarlyTemperature = false;
   static constexpr int kRowsPerBlock = MR * 16;
   static constexpr size_t kSmemBytes = static_cast<size_t>(NW) * MR * NT * kWave * sizeof(f32x4);
   static constexpr int kWavesPerSimd = 1;
@@ -203,6 +207,8 @@ struct KSplitLoop {
 template <int MR_, int NT_, int NW_, int KC, int P, bool NTL, int WB_ = 1, int BR = 0>
 struct LdsLoop {
   static constexpr int MR = MR_, NT = NT_, NW = NW_;
+  // the epilogue's per-row temperatures are loaded after the main loop
+  static constexpr bool kEarlyTemperature = false;
   // The block's waves form WR row groups x WB batch groups: with WB > 1 each
   // W row group is computed by WB waves against different batch rows, which
   // halves (WB = 2) the LDS bytes read per MFMA for the same accumulators.
@@ -372,6 +378,9 @@ struct LdsLoop {
 template <int MR_, int NT_, int NW_, int KC, int P, int S, int BR, int G = 1>
 struct DmaLoop {
   static constexpr int MR = MR_, NT = NT_, NW = NW_;
+  // registers to spare: the epilogue's per-row temperatures are loaded
+  // before the main loop, hiding their latency entirely
+  static constexpr bool kEarlyTemperature = true;
   static constexpr int kRowsPerBlock = MR * 16 * NW;
   static constexpr int kBlockCols = NT * 16;
   static constexpr int KS = KC / 32;                 // MFMA k-steps per chunk
