@@ -389,6 +389,7 @@ const FusedConfig kConfigs[] = {
     FS_DMA(4, 8, 8, 64, 4, 3, 4),
     FS_DMAG(2, 16, 8, 64, 8, 3, 4, 2),
     FS_DMAG(2, 8, 8, 64, 4, 4, 4, 2),
+    FS_DMAG(2, 16, 8, 128, 4, 2, 4, 2),
     FS_KSPLIT(2, 1, 4, 8, 0),
     FS_KSPLIT(4, 2, 4, 4, 0),
     FS_STREAM(1, 1, 4, 8, 0),
