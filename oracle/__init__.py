@@ -74,6 +74,16 @@ def _load():
             fn = getattr(lib, name)
             fn.argtypes = [ctypes.c_void_p, ctypes.c_int64, ctypes.c_void_p]
             fn.restype = None
+        vp, i32, u32, u64 = ctypes.c_void_p, ctypes.c_int32, ctypes.c_uint32, ctypes.c_uint64
+        lib.oracle_group_gumbel.argtypes = [u64, u64, u32, u32]
+        lib.oracle_group_gumbel.restype = ctypes.c_float
+        lib.oracle_sample_lse.argtypes = [vp, vp, i32, i32, i32, vp, u64, u64, vp, i32,
+                                          vp, vp, vp, vp]
+        lib.oracle_sample_lse.restype = None
+        lib.oracle_merge_lse.argtypes = [vp, vp, vp, i32, i32, vp, u64, u64, vp, vp, vp, vp]
+        lib.oracle_merge_lse.restype = None
+        lib.oracle_lse_logits.argtypes = [vp, i32, vp, i32, vp]
+        lib.oracle_lse_logits.restype = None
         lib.oracle_max_threads.argtypes = []
         lib.oracle_max_threads.restype = ctypes.c_int
         _lib = lib
@@ -220,3 +230,64 @@ def merge(val, ids):
     out_val = np.empty(B, np.float32)
     _load().oracle_merge(_ptr(val), _ptr(ids), P, B, _ptr(out_id), _ptr(out_val))
     return out_id, out_val
+
+
+# ---------------------------------------------------------------------------
+# Grouped (hierarchical) sampler: oracle.c, "Grouped (hierarchical) sampler".
+# ---------------------------------------------------------------------------
+def group_gumbel(seed, step, row, p):
+    """Gumbel draw of group p for a batch row (disjoint from token noise)."""
+    return float(_load().oracle_group_gumbel(int(seed), int(step), int(row), int(p)))
+
+
+def sample_lse(h, W, T, seed, step, vocab_offset=0, rows=None):
+    """As ``sample``, plus the log-sum-exp of each row's scaled logits over
+    the slice (greedy rows: the largest logit).  Returns (ids, val, gap, lse)."""
+    h = _c(h, np.uint16)
+    W = _c(W, np.uint16)
+    T = _c(T, np.float32)
+    B, D = h.shape
+    V, D2 = W.shape
+    assert D == D2 and T.shape == (B,)
+    r = None if rows is None else _c(rows, np.int32)
+    n = B if r is None else r.size
+    ids = np.empty(n, np.int32)
+    val = np.empty(n, np.float32)
+    gap = np.empty(n, np.float32)
+    lse = np.empty(n, np.float32)
+    if n:
+        _load().oracle_sample_lse(_ptr(h), _ptr(W), D, V, int(vocab_offset), _ptr(T),
+                                  int(seed), int(step), _ptr(r), n, _ptr(ids), _ptr(val),
+                                  _ptr(gap), _ptr(lse))
+    return ids, val, gap, lse
+
+
+def lse_logits(z, T):
+    """Log-sum-exp of fixed fp32 logits z (R x V), one per row."""
+    z = _c(z, np.float32)
+    T = _c(T, np.float32)
+    R, V = z.shape
+    assert T.shape == (R,)
+    out = np.empty(R, np.float32)
+    _load().oracle_lse_logits(_ptr(z), V, _ptr(T), R, _ptr(out))
+    return out
+
+
+def merge_lse(val, ids, lse, T, seed, step):
+    """Grouped merge of P x B partials (val, ids, lse), group p in row p.
+    Returns (ids, val, total_lse, key_gap) per batch row."""
+    val = _c(val, np.float32)
+    ids = _c(ids, np.int32)
+    lse = _c(lse, np.float32)
+    T = _c(T, np.float32)
+    assert val.shape == ids.shape == lse.shape and val.ndim == 2
+    P, B = val.shape
+    assert T.shape == (B,)
+    out_id = np.empty(B, np.int32)
+    out_val = np.empty(B, np.float32)
+    out_lse = np.empty(B, np.float32)
+    out_gap = np.empty(B, np.float32)
+    _load().oracle_merge_lse(_ptr(val), _ptr(ids), _ptr(lse), P, B, _ptr(T), int(seed),
+                             int(step), _ptr(out_id), _ptr(out_val), _ptr(out_lse),
+                             _ptr(out_gap))
+    return out_id, out_val, out_lse, out_gap

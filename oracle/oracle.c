@@ -39,6 +39,7 @@
 #include <omp.h>
 #include <stddef.h>
 #include <stdint.h>
+#include <stdlib.h>
 #include <string.h>
 
 #define ORACLE_EXPORT __attribute__((visibility("default")))
@@ -289,5 +290,141 @@ ORACLE_EXPORT void oracle_merge(const float* val, const int32_t* id, int32_t P,
     }
     out_id[b] = best_id;
     out_val[b] = best;
+  }
+}
+
+/* ---------------------------------------------------------------------- */
+/* Grouped (hierarchical) sampler                                           */
+/* ---------------------------------------------------------------------- */
+/* The categorical distribution factorises over any partition of the
+ * vocabulary into groups G: P(i) = P(G) * P(i | G), with P(G) proportional
+ * to exp(LSE_G), LSE_G = log sum_{i in G} exp(z_i / T) (arXiv abstract page
+ * and wiki summary, "Key claims": grouped variants for online and
+ * tensor-parallel settings are exact by this hierarchical factorisation).
+ * The pages give no formulas; the reading built here:
+ *   - a group's own sample is its Gumbel-max winner over the token noise
+ *     field above (oracle_sample on the group's slice), distributed as
+ *     P(i | G);
+ *   - the group is chosen by a second Gumbel-max, argmax_G (LSE_G + gamma_G),
+ *     with gamma_G a standard Gumbel draw independent of the token noise;
+ *   - the output is the chosen group's sample, plus the total
+ *     log-sum-exp over the groups (the normaliser of the whole row).
+ * Greedy rows (T not > 0) have a point-mass distribution: LSE_G is the
+ * group's largest logit and the group choice takes no noise, which selects
+ * the group holding the global argmax.                                     */
+
+/* Gumbel draw of group p for batch row `row`: the token generator with the
+ * same key, on counter (2^31 | p, row, step low, step high), output word 0.
+ * Token counters have word 0 = gv / 4 < 2^29, so the two streams never
+ * share a counter.                                                         */
+ORACLE_EXPORT float oracle_group_gumbel(uint64_t seed, uint64_t step, uint32_t row,
+                                        uint32_t p) {
+  uint32_t ctr[4] = {0x80000000u | p, row, (uint32_t)step, (uint32_t)(step >> 32)};
+  uint32_t key[2] = {(uint32_t)seed, (uint32_t)(seed >> 32)};
+  uint32_t out[4];
+  oracle_philox4x32_10(ctr, key, out);
+  return oracle_gumbel(out[0]);
+}
+
+/* As oracle_sample, plus per listed row the log-sum-exp of the slice's
+ * scaled logits, log sum_v exp(z_v * (1/T)) with the fp32 reciprocal of
+ * T, evaluated in fp64 around the slice maximum and rounded once to fp32;
+ * for greedy rows the slice's largest logit.                              */
+ORACLE_EXPORT void oracle_sample_lse(const uint16_t* h, const uint16_t* W, int32_t D,
+                                     int32_t V, int32_t vocab_offset, const float* T,
+                                     uint64_t seed, uint64_t step, const int32_t* rows,
+                                     int32_t n_rows, int32_t* out_id, float* out_val,
+                                     float* out_gap, float* out_lse) {
+#pragma omp parallel for schedule(dynamic, 1)
+  for (int32_t i = 0; i < n_rows; ++i) {
+    int32_t b = rows ? rows[i] : i;
+    float Tb = T[b];
+    int greedy = is_greedy(Tb);
+    float inv_T = greedy ? 1.0f : 1.0f / Tb;
+    running_max r;
+    rm_init(&r);
+    double zmax = -INFINITY;
+    double* scaled = (double*)malloc(sizeof(double) * (size_t)V);
+    for (int32_t v = 0; v < V; ++v) {
+      float z = oracle_logit(h + (size_t)b * D, W + (size_t)v * D, D);
+      int32_t gv = vocab_offset + v;
+      rm_push(&r, score(z, Tb, inv_T, seed, step, (uint32_t)b, (uint32_t)gv), gv);
+      scaled[v] = greedy ? (double)z : (double)z * (double)inv_T;
+      if (scaled[v] > zmax) zmax = scaled[v];
+    }
+    double lse = zmax;
+    if (!greedy) {
+      double sum = 0.0;
+      for (int32_t v = 0; v < V; ++v) sum += exp(scaled[v] - zmax);
+      lse = zmax + log(sum);
+    }
+    free(scaled);
+    out_id[i] = r.best_id;
+    out_val[i] = r.best;
+    out_gap[i] = r.best - r.second;
+    out_lse[i] = (float)lse;
+  }
+}
+
+/* Grouped merge.  Partials are P x B, part-major (val, id, lse), group p in
+ * slot p.  Per row b: the group key is lse_p + gamma_p, an fp32 add of the
+ * fp32 group draw (greedy rows: lse_p alone); the largest key wins, ties to
+ * the smaller p.  Outputs the winner's (id, val), the total log-sum-exp
+ * log sum_p exp(lse_p) (fp64 around the maximum, rounded once; greedy rows:
+ * the largest lse_p) and the gap between the two largest keys.            */
+ORACLE_EXPORT void oracle_merge_lse(const float* val, const int32_t* id, const float* lse,
+                                    int32_t P, int32_t B, const float* T, uint64_t seed,
+                                    uint64_t step, int32_t* out_id, float* out_val,
+                                    float* out_lse, float* out_gap) {
+  for (int32_t b = 0; b < B; ++b) {
+    int greedy = is_greedy(T[b]);
+    int32_t best_p = -1;
+    float best_key = -INFINITY, second_key = -INFINITY;
+    double lmax = -INFINITY;
+    for (int32_t p = 0; p < P; ++p) {
+      float l = lse[(size_t)p * B + b];
+      float key = greedy ? l : l + oracle_group_gumbel(seed, step, (uint32_t)b, (uint32_t)p);
+      if (best_p < 0 || key > best_key) {
+        if (best_p >= 0) second_key = best_key;
+        best_key = key;
+        best_p = p;
+      } else if (key > second_key) {
+        second_key = key;
+      }
+      if ((double)l > lmax) lmax = (double)l;
+    }
+    double total = lmax;
+    if (!greedy) {
+      double sum = 0.0;
+      for (int32_t p = 0; p < P; ++p) sum += exp((double)lse[(size_t)p * B + b] - lmax);
+      total = lmax + log(sum);
+    }
+    out_id[b] = id[(size_t)best_p * B + b];
+    out_val[b] = val[(size_t)best_p * B + b];
+    out_lse[b] = (float)total;
+    out_gap[b] = best_key - second_key;
+  }
+}
+
+/* Log-sum-exp of fixed fp32 logits, one per row of z (R x V), with the same
+ * scaling and evaluation as oracle_sample_lse.                            */
+ORACLE_EXPORT void oracle_lse_logits(const float* z, int32_t V, const float* T, int32_t R,
+                                     float* out_lse) {
+  for (int32_t i = 0; i < R; ++i) {
+    int greedy = is_greedy(T[i]);
+    float inv_T = greedy ? 1.0f : 1.0f / T[i];
+    double zmax = -INFINITY;
+    for (int32_t v = 0; v < V; ++v) {
+      double s = greedy ? (double)z[(size_t)i * V + v] : (double)z[(size_t)i * V + v] * (double)inv_T;
+      if (s > zmax) zmax = s;
+    }
+    double lse = zmax;
+    if (!greedy) {
+      double sum = 0.0;
+      for (int32_t v = 0; v < V; ++v)
+        sum += exp((double)z[(size_t)i * V + v] * (double)inv_T - zmax);
+      lse = zmax + log(sum);
+    }
+    out_lse[i] = (float)lse;
   }
 }
