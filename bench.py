@@ -65,7 +65,9 @@ def kernel_sources_sha256():
     import hashlib
     csrc = os.path.join(ROOT, "lm_head_exact_amd", "csrc")
     h = hashlib.sha256()
-    for name in ("fs_device.hpp", "fs_internal.hpp", "fs_mma.hpp", "fs_fused.hip"):
+    for name in ("fs_device.hpp", "fs_internal.hpp", "fs_mma.hpp", "fs_sampler.hpp",
+                 "fs_fused.hip", "fs_configs_small.hip", "fs_configs_lds.hip",
+                 "fs_configs_dma_a.hip", "fs_configs_dma_b.hip"):
         h.update(name.encode())
         h.update(open(os.path.join(csrc, name), "rb").read())
     return h.hexdigest()

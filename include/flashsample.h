@@ -112,6 +112,42 @@ FS_API fs_status fs_sample_partial(const void* h, const void* W, int32_t B, int3
 FS_API fs_status fs_merge(const float* partial_val, const int32_t* partial_idx, int32_t P,
                    int32_t B, int32_t* out_ids, float* out_maxval, void* stream);
 
+/* Grouped (hierarchical) sampler, one vocabulary group per call (arXiv
+ * abstract page and wiki summary, "Key claims": grouped variants for online
+ * and tensor-parallel settings are exact by hierarchical factorisation of
+ * the categorical distribution; wiki summary, "Method", last paragraph: the
+ * online, chunked setting).  As fs_sample_partial, plus
+ *   partial_lse  fp32 [B], device: per row the log-sum-exp of the group's
+ *                scaled logits, log sum_v exp(z_v * (1/T)); for greedy rows
+ *                (T not > 0) the group's largest logit.
+ * partial_val / partial_idx are bit-identical to fs_sample_partial's on the
+ * same inputs.  Same workspace (fs_workspace_bytes) and errors. */
+FS_API fs_status fs_sample_partial_lse(const void* h, const void* W, int32_t B, int32_t D,
+                                int32_t V, int32_t vocab_offset, const float* temperature,
+                                uint64_t seed, uint64_t step, float* partial_val,
+                                int32_t* partial_idx, float* partial_lse, void* workspace,
+                                size_t workspace_bytes, void* stream);
+
+/* Grouped merge: the categorical distribution factorises as
+ * P(i) = P(G) P(i | G) with P(G) proportional to exp(LSE_G), and each
+ * group's partial already holds a sample of P(i | G).
+ *   partial_val, partial_idx, partial_lse  [P][B] (part-major), from
+ *                fs_sample_partial_lse, group p in slot p
+ *   temperature  fp32 [B], device (greedy rows as in fs_sample)
+ *   seed, step   key of the group draws: gamma_p is the Gumbel value of
+ *                Philox-4x32-10 word 0 at counter (2^31 | p, row, step low,
+ *                step high) under key (seed low, seed high), a counter the
+ *                token noise never uses
+ * Per row b the group p* = argmax_p (lse_p + gamma_p) (greedy rows:
+ * argmax_p lse_p), ties to the smaller p; out_ids[b] / out_maxval[b] are
+ * that group's partial, out_lse[b] the row's total log-sum-exp over the
+ * groups (greedy rows: the largest lse_p).  All pointers device, 4-byte
+ * aligned; P >= 1, B >= 0. */
+FS_API fs_status fs_merge_lse(const float* partial_val, const int32_t* partial_idx,
+                       const float* partial_lse, int32_t P, int32_t B,
+                       const float* temperature, uint64_t seed, uint64_t step,
+                       int32_t* out_ids, float* out_maxval, float* out_lse, void* stream);
+
 /* The standard unfused decode step the method replaces (wiki summary,
  * "Method", first paragraph): (1) matmul writing fp32 logits [B][V] to
  * device memory, (2) softmax of z / T writing probabilities, (3)+(4)

@@ -6,7 +6,7 @@ kernels, declared in ``include/flashsample.h``); the functions exported here
 only marshal torch tensors into that library.  The library is loaded on first
 use and a missing build raises instead of falling back to anything else.
 """
-_BINDING_NAMES = ("sample", "sample_partial", "merge", "sample_unfused", "workspace_bytes",
+_BINDING_NAMES = ("sample", "sample_partial", "merge", "sample_partial_lse", "merge_lse", "sample_unfused", "workspace_bytes",
                   "unfused_workspace_bytes", "library_path", "debug_noise", "debug_gumbel",
                   "num_configs", "config_name", "profile_enable", "profile_read", "force_config", "selected_config",
                   "FlashSampleError", "alloc_workspace")

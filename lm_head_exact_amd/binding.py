@@ -58,6 +58,9 @@ def lib():
         ("fs_sample_partial", sample_args, ctypes.c_int),
         ("fs_sample_unfused", sample_args, ctypes.c_int),
         ("fs_merge", [vp, vp, i32, i32, vp, vp, vp], ctypes.c_int),
+        ("fs_sample_partial_lse", [vp, vp, i32, i32, i32, i32, vp, u64, u64, vp, vp, vp, vp,
+                                   sz, vp], ctypes.c_int),
+        ("fs_merge_lse", [vp, vp, vp, i32, i32, vp, u64, u64, vp, vp, vp, vp], ctypes.c_int),
         ("fs_debug_noise", [u64, u64, u32, u32, i64, vp, vp, vp], ctypes.c_int),
         ("fs_debug_gumbel", [vp, i64, vp, vp], ctypes.c_int),
         ("fs_num_configs", [], i32),
@@ -167,6 +170,61 @@ def sample_partial(h, W, temperature, seed, step, vocab_offset, partial_val, par
     _sample_common("fs_sample_partial", h, W, temperature, seed, step, vocab_offset,
                    partial_val, partial_idx, workspace, workspace_bytes)
     return partial_val, partial_idx
+
+
+def sample_partial_lse(h, W, temperature, seed, step, vocab_offset, partial_val, partial_idx,
+                       partial_lse, workspace=None):
+    """One vocabulary group's per-row (max, global argmax) and log-sum-exp of the
+    scaled logits into partial_val / partial_idx / partial_lse (B each)."""
+    _req(partial_val, "partial_val", torch.float32, 1)
+    _req(partial_idx, "partial_idx", torch.int32, 1)
+    _req(partial_lse, "partial_lse", torch.float32, 1)
+    _req(h, "h", torch.bfloat16, 2)
+    _req(W, "W", torch.bfloat16, 2)
+    _req(temperature, "temperature", torch.float32, 1)
+    B, D = h.shape
+    V, D2 = W.shape
+    if D2 != D:
+        raise ValueError(f"h is B x {D} but W is V x {D2}")
+    if not (temperature.shape[0] == partial_val.shape[0] == partial_idx.shape[0] ==
+            partial_lse.shape[0] == B):
+        raise ValueError("temperature and the partials must have B entries")
+    devs = {t.device for t in (h, W, temperature, partial_val, partial_idx, partial_lse)}
+    if len(devs) != 1:
+        raise ValueError("all tensors must be on one device")
+    if workspace is None:
+        workspace = alloc_workspace(workspace_bytes(B, D, V), h.device)
+    _check(lib().fs_sample_partial_lse(
+        _ptr(h), _ptr(W), B, D, V, int(vocab_offset), _ptr(temperature),
+        int(seed) & (2**64 - 1), int(step) & (2**64 - 1), _ptr(partial_val), _ptr(partial_idx),
+        _ptr(partial_lse), _ptr(workspace), workspace.numel() * workspace.element_size(),
+        _stream(h.device)))
+    return partial_val, partial_idx, partial_lse
+
+
+def merge_lse(partial_val, partial_idx, partial_lse, temperature, seed, step, out=None):
+    """Grouped merge of P x B group partials: returns (ids int32[B], maxval fp32[B],
+    total log-sum-exp fp32[B])."""
+    _req(partial_val, "partial_val", torch.float32, 2)
+    _req(partial_idx, "partial_idx", torch.int32, 2)
+    _req(partial_lse, "partial_lse", torch.float32, 2)
+    _req(temperature, "temperature", torch.float32, 1)
+    if not (partial_val.shape == partial_idx.shape == partial_lse.shape):
+        raise ValueError("the partials must have the same shape")
+    P, B = partial_val.shape
+    if temperature.shape[0] != B:
+        raise ValueError("temperature must have B entries")
+    dev = partial_val.device
+    if out is None:
+        out = (torch.empty(B, dtype=torch.int32, device=dev),
+               torch.empty(B, dtype=torch.float32, device=dev),
+               torch.empty(B, dtype=torch.float32, device=dev))
+    ids, val, lse = out
+    _check(lib().fs_merge_lse(_ptr(partial_val), _ptr(partial_idx), _ptr(partial_lse), P, B,
+                              _ptr(temperature), int(seed) & (2**64 - 1),
+                              int(step) & (2**64 - 1), _ptr(ids), _ptr(val), _ptr(lse),
+                              _stream(dev)))
+    return ids, val, lse
 
 
 def sample_unfused(h, W, temperature, seed, step, vocab_offset=0, out=None, workspace=None):

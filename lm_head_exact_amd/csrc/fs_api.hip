@@ -68,9 +68,16 @@ fs_status check_sample_args(const void* h, const void* W, int32_t B, int32_t D, 
   return FS_OK;
 }
 
+// Most vocabulary blocks any configuration launches: blocks of at least
+// kMinRowsPerBlock rows over a grid of V rows shifted by vocab_offset mod 4
+// (< 4) rows.
+size_t max_splits(int32_t V) {
+  return (static_cast<size_t>(V) + 3 + fs::kMinRowsPerBlock - 1) / fs::kMinRowsPerBlock;
+}
+
+// Workspace: per-tile partial values, ids and log-sum-exps, each [B][S].
 size_t fused_workspace(int32_t B, int32_t V) {
-  const size_t S = (static_cast<size_t>(V) + fs::kMinRowsPerBlock - 1) / fs::kMinRowsPerBlock;
-  return fs::round_up(sizeof(float) * B * S, 256) + fs::round_up(sizeof(int32_t) * B * S, 256);
+  return 3 * fs::round_up(sizeof(float) * B * max_splits(V), 256);
 }
 
 // Event pairs around fused-kernel launches (fs_profile_enable / _read).
@@ -93,11 +100,14 @@ int choose_config(int32_t B, int32_t D, int32_t V) {
   return forced >= 0 ? forced : fs::fused_auto_config(B, D, V);
 }
 
-// Shared body of fs_sample / fs_sample_partial.
+// Shared body of fs_sample / fs_sample_partial / fs_sample_partial_lse
+// (out_lse non-null: also the per-row log-sum-exp of the scaled logits).
 fs_status run_fused(const void* h, const void* W, int32_t B, int32_t D, int32_t V,
                     int32_t vocab_offset, const float* temperature, uint64_t seed,
-                    uint64_t step, int32_t* out_ids, float* out_val, void* workspace,
-                    size_t workspace_bytes, void* stream, const char* who) {
+                    uint64_t step, int32_t* out_ids, float* out_val, float* out_lse,
+                    void* workspace, size_t workspace_bytes, void* stream, const char* who) {
+  if (out_lse && !aligned(out_lse, 4))
+    return fail(FS_ERR_INVALID_ARG, "%s: partial_lse must be 4-byte aligned", who);
   fs_status s = check_sample_args(h, W, B, D, V, vocab_offset, temperature, out_ids, out_val,
                                   workspace);
   if (s != FS_OK || B == 0) return s;
@@ -109,7 +119,7 @@ fs_status run_fused(const void* h, const void* W, int32_t B, int32_t D, int32_t 
   if (!fs::fused_config_supports(cfg, B, D))
     return fail(FS_ERR_UNSUPPORTED, "%s: forced configuration %s does not support B=%d, D=%d",
                 who, fs::fused_config_name(cfg), B, D);
-  const size_t S = (static_cast<size_t>(V) + fs::kMinRowsPerBlock - 1) / fs::kMinRowsPerBlock;
+  const size_t S = max_splits(V);
   fs::SampleArgs a;
   a.h = static_cast<const __bf16*>(h);
   a.W = static_cast<const __bf16*>(W);
@@ -121,8 +131,10 @@ fs_status run_fused(const void* h, const void* W, int32_t B, int32_t D, int32_t 
   a.seed = seed;
   a.step = step;
   a.part_val = static_cast<float*>(workspace);
-  a.part_idx = reinterpret_cast<int32_t*>(static_cast<char*>(workspace) +
-                                          fs::round_up(sizeof(float) * B * S, 256));
+  const size_t region = fs::round_up(sizeof(float) * B * S, 256);
+  a.part_idx = reinterpret_cast<int32_t*>(static_cast<char*>(workspace) + region);
+  a.part_lse = out_lse ? reinterpret_cast<float*>(static_cast<char*>(workspace) + 2 * region)
+                       : nullptr;
   a.S = 0;
   const hipStream_t st = static_cast<hipStream_t>(stream);
   hipError_t e;
@@ -143,7 +155,9 @@ fs_status run_fused(const void* h, const void* W, int32_t B, int32_t D, int32_t 
     e = fs::launch_fused(cfg, a, st);
     if (e != hipSuccess) return hip_fail(e, "fused sampler launch");
   }
-  e = fs::launch_merge(a.part_val, a.part_idx, a.S, B, 1, a.S, out_ids, out_val, st);
+  e = out_lse ? fs::launch_merge_tiles_lse(a.part_val, a.part_idx, a.part_lse, a.S, B,
+                                           temperature, out_ids, out_val, out_lse, st)
+              : fs::launch_merge(a.part_val, a.part_idx, a.S, B, 1, a.S, out_ids, out_val, st);
   if (e != hipSuccess) return hip_fail(e, "merge launch");
   if (getenv("FS_LOG"))
     fprintf(stderr, "[flashsample] %s B=%d D=%d V=%d config=%s splits=%d\n", who, B, D, V,
@@ -170,7 +184,7 @@ fs_status fs_sample(const void* h, const void* W, int32_t B, int32_t D, int32_t 
                     uint64_t step, int32_t* out_ids, float* out_maxval, void* workspace,
                     size_t workspace_bytes, void* stream) {
   return run_fused(h, W, B, D, V, vocab_offset, temperature, seed, step, out_ids, out_maxval,
-                   workspace, workspace_bytes, stream, "fs_sample");
+                   nullptr, workspace, workspace_bytes, stream, "fs_sample");
 }
 
 fs_status fs_sample_partial(const void* h, const void* W, int32_t B, int32_t D, int32_t V,
@@ -178,7 +192,41 @@ fs_status fs_sample_partial(const void* h, const void* W, int32_t B, int32_t D, 
                             uint64_t step, float* partial_val, int32_t* partial_idx,
                             void* workspace, size_t workspace_bytes, void* stream) {
   return run_fused(h, W, B, D, V, vocab_offset, temperature, seed, step, partial_idx,
-                   partial_val, workspace, workspace_bytes, stream, "fs_sample_partial");
+                   partial_val, nullptr, workspace, workspace_bytes, stream, "fs_sample_partial");
+}
+
+fs_status fs_sample_partial_lse(const void* h, const void* W, int32_t B, int32_t D, int32_t V,
+                                int32_t vocab_offset, const float* temperature, uint64_t seed,
+                                uint64_t step, float* partial_val, int32_t* partial_idx,
+                                float* partial_lse, void* workspace, size_t workspace_bytes,
+                                void* stream) {
+  if (B > 0 && !partial_lse) return fail(FS_ERR_INVALID_ARG, "null pointer argument");
+  return run_fused(h, W, B, D, V, vocab_offset, temperature, seed, step, partial_idx,
+                   partial_val, partial_lse, workspace, workspace_bytes, stream,
+                   "fs_sample_partial_lse");
+}
+
+fs_status fs_merge_lse(const float* partial_val, const int32_t* partial_idx,
+                       const float* partial_lse, int32_t P, int32_t B,
+                       const float* temperature, uint64_t seed, uint64_t step,
+                       int32_t* out_ids, float* out_maxval, float* out_lse, void* stream) {
+  if (P < 1) return fail(FS_ERR_INVALID_ARG, "P must be >= 1 (got %d)", P);
+  if (B < 0) return fail(FS_ERR_INVALID_ARG, "B must be >= 0 (got %d)", B);
+  if (B == 0) return FS_OK;
+  if (!partial_val || !partial_idx || !partial_lse || !temperature || !out_ids || !out_maxval ||
+      !out_lse)
+    return fail(FS_ERR_INVALID_ARG, "null pointer argument");
+  if (!aligned(partial_val, 4) || !aligned(partial_idx, 4) || !aligned(partial_lse, 4) ||
+      !aligned(temperature, 4) || !aligned(out_ids, 4) || !aligned(out_maxval, 4) ||
+      !aligned(out_lse, 4))
+    return fail(FS_ERR_INVALID_ARG, "pointers must be 4-byte aligned");
+  if (static_cast<int64_t>(P) * B > (int64_t{1} << 40))
+    return fail(FS_ERR_INVALID_ARG, "P * B too large");
+  hipError_t e = fs::launch_merge_groups_lse(partial_val, partial_idx, partial_lse, P, B,
+                                             temperature, seed, step, out_ids, out_maxval,
+                                             out_lse, static_cast<hipStream_t>(stream));
+  if (e != hipSuccess) return hip_fail(e, "grouped merge launch");
+  return FS_OK;
 }
 
 fs_status fs_merge(const float* partial_val, const int32_t* partial_idx, int32_t P, int32_t B,
@@ -221,6 +269,7 @@ fs_status fs_sample_unfused(const void* h, const void* W, int32_t B, int32_t D, 
   a.seed = seed;
   a.step = step;
   a.part_val = nullptr;
+  a.part_lse = nullptr;
   a.part_idx = nullptr;
   a.S = 0;
   hipError_t e = fs::launch_unfused(a, out_ids, out_maxval, workspace,

@@ -1,0 +1,18 @@
+// fs_configs_dma_b.hip -- further DMA-staged configurations of the fused sampler (tuning sweeps)
+// (one of several translation units, compiled in parallel).
+#include "fs_sampler.hpp"
+
+namespace fs {
+
+int fused_configs_dma_b(const FusedConfig** out) {
+  static const FusedConfig k[] = {
+      FS_DMA(2, 16, 8, 64, 4, 4, 4),
+      FS_DMA(4, 8, 8, 64, 4, 3, 4),
+      FS_DMAG(2, 16, 8, 64, 8, 3, 4, 2),
+      FS_DMAG(2, 8, 8, 64, 4, 4, 4, 2),
+  };
+  *out = k;
+  return static_cast<int>(sizeof(k) / sizeof(k[0]));
+}
+
+}  // namespace fs

@@ -146,6 +146,45 @@ struct ArgMax {
   }
 };
 
+// ---------------------------------------------------------------------------
+// Running log-sum-exp, log sum_i exp(t_i), of a stream of scaled logits t_i,
+// kept as (m, s) with m the running maximum and s = sum_i exp(t_i - m)
+// (online normaliser: the maximum is folded in as it grows).  Masked
+// entries are pushed as -FLT_MAX: finite, so no inf - inf arises, and their
+// exponential underflows to 0 beside any real entry.  exp is the hardware
+// exp2 of x log2(e).
+// ---------------------------------------------------------------------------
+struct LseAcc {
+  float m, s;
+  static constexpr float kMasked = -3.402823466e38f;
+  __device__ __forceinline__ static float ex(float x) {
+    return __builtin_amdgcn_exp2f(x * 1.44269504088896341f);
+  }
+  __device__ __forceinline__ void init() {
+    m = kMasked;
+    s = 0.0f;
+  }
+  __device__ __forceinline__ void push4(f32x4 t) {
+    const float nm = fmaxf(m, fmaxf(fmaxf(t[0], t[1]), fmaxf(t[2], t[3])));
+    s = s * ex(m - nm) + ((ex(t[0] - nm) + ex(t[1] - nm)) + (ex(t[2] - nm) + ex(t[3] - nm)));
+    m = nm;
+  }
+  __device__ __forceinline__ void merge(float om, float os) {
+    const float nm = fmaxf(m, om);
+    s = s * ex(m - nm) + os * ex(om - nm);
+    m = nm;
+  }
+  __device__ __forceinline__ void xor_reduce(int mask) {
+    const float om = __shfl_xor(m, mask, kWave);
+    const float os = __shfl_xor(s, mask, kWave);
+    merge(om, os);
+  }
+  // log-sum-exp; greedy rows report the maximum (their distribution's mode)
+  __device__ __forceinline__ float value(bool greedy) const {
+    return greedy ? m : m + __builtin_amdgcn_logf(s) * 0.693147180559945309f;
+  }
+};
+
 // Row temperature -> (greedy flag, fp32 reciprocal).  Greedy when T is not a
 // positive number (0, -0, negative, NaN): the T -> 0 limit of the sampler.
 __device__ __forceinline__ bool row_is_greedy(float T) { return !(T > 0.0f); }
@@ -161,32 +200,31 @@ __device__ __forceinline__ float perturbed_score(float z, float inv_t, float g) 
 }
 
 // Pushes the scores of four consecutive logits z (local vocabulary rows
-// v0 .. v0+3, global ids gv0 .. gv0+3, batch row `row`) into `best`.  Rows
-// at or past V score -inf and never win; greedy rows score the logit itself.
-// Everything is computed on every lane and selected, without branches: the
-// lanes of a wave hold different batch rows, so a branch would serialise.
-// ALIGN4: gv0 % 4 == 0, so the four ids share one Philox block.
-template <bool ALIGN4>
+// v0 .. v0+3, global ids gv0 .. gv0+3 with gv0 % 4 == 0, batch row `row`)
+// into `best`; the four ids share one Philox block.  Rows outside [0, V)
+// score -inf and never win; greedy rows score the logit itself.  Everything
+// is computed on every lane and selected, without branches: the lanes of a
+// wave hold different batch rows, so a branch would serialise.  With LSE,
+// also folds the scaled logits z / T (greedy rows: z) of the valid rows into
+// `lse`.
+template <bool LSE = false>
 __device__ __forceinline__ void push_four(ArgMax& best, f32x4 z, int v0, int32_t V, uint32_t gv0,
                                           uint32_t row, uint64_t step, bool greedy,
-                                          float inv_t, const Philox& philox) {
-  const u32x4 w0 = philox(noise_counter(gv0, row, step));
-  u32x4 w1 = w0;
-  if (!ALIGN4) w1 = philox(noise_counter(gv0 + 4u, row, step));
+                                          float inv_t, const Philox& philox,
+                                          LseAcc* lse = nullptr) {
+  const u32x4 w = philox(noise_counter(gv0, row, step));
+  f32x4 t;
   static_for<4>([&](auto rc) FS_INLINE {
     constexpr int r = decltype(rc)::value;
-    uint32_t x;
-    if (ALIGN4) {
-      x = w0[r];
-    } else {
-      const uint32_t q = (gv0 & 3u) + r;  // word index across the two blocks
-      x = q < 4u ? pick_word(w0, q) : pick_word(w1, q - 4u);
-    }
-    const float noisy = perturbed_score(z[r], inv_t, gumbel_from_bits(x));
+    const float scaled = __fmul_rn(z[r], inv_t);
+    const float noisy = __fadd_rn(scaled, gumbel_from_bits(w[r]));
+    const bool valid = static_cast<uint32_t>(v0 + r) < static_cast<uint32_t>(V);
     float s = greedy ? z[r] : noisy;
-    s = v0 + r < V ? s : -__builtin_inff();
+    s = valid ? s : -__builtin_inff();
     best.push_ascending(s, static_cast<int32_t>(gv0 + r));
+    if (LSE) t[r] = valid ? (greedy ? z[r] : scaled) : LseAcc::kMasked;
   });
+  if (LSE) lse->push4(t);
 }
 
 }  // namespace fs

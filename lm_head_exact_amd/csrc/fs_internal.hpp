@@ -16,8 +16,24 @@ struct SampleArgs {
   uint64_t seed, step;
   float* part_val;    // [B][S] per-block partial maxima
   int32_t* part_idx;  // [B][S] their global ids
+  float* part_lse;    // [B][S] per-block log-sum-exp of z / T (grouped sampler), or null
   int32_t S;          // number of vocabulary blocks (set by the launcher)
 };
+
+// One fused-sampler configuration (a main-loop policy and its tile shape).
+struct FusedConfig {
+  const char* name;
+  int rows_per_block;
+  hipError_t (*launch)(SampleArgs&, hipStream_t);
+  bool (*supports)(int32_t B, int32_t D);
+  int order;  // configurations of equal order sum the contraction identically
+};
+
+// Configuration lists of the translation units fs_configs_*.hip.
+int fused_configs_small(const FusedConfig** out);
+int fused_configs_lds(const FusedConfig** out);
+int fused_configs_dma_a(const FusedConfig** out);
+int fused_configs_dma_b(const FusedConfig** out);
 
 // ---- fused sampler (fs_fused.hip) ----
 int num_fused_configs();
@@ -36,6 +52,18 @@ hipError_t launch_fused(int id, SampleArgs& a, hipStream_t stream);
 hipError_t launch_merge(const float* val, const int32_t* idx, int32_t P, int32_t B,
                         int64_t stride_p, int64_t stride_b, int32_t* out_ids,
                         float* out_val, hipStream_t stream);
+
+// Per-row argmax and log-sum-exp over the S tile partials of one slice
+// (element (b, t) at b * S + t).
+hipError_t launch_merge_tiles_lse(const float* val, const int32_t* idx, const float* lse,
+                                  int32_t S, int32_t B, const float* temperature,
+                                  int32_t* out_ids, float* out_val, float* out_lse,
+                                  hipStream_t stream);
+// Grouped merge over P group partials, part-major (element (p, b) at p * B + b).
+hipError_t launch_merge_groups_lse(const float* val, const int32_t* idx, const float* lse,
+                                   int32_t P, int32_t B, const float* temperature,
+                                   uint64_t seed, uint64_t step, int32_t* out_ids,
+                                   float* out_val, float* out_lse, hipStream_t stream);
 
 hipError_t launch_debug_noise(uint64_t seed, uint64_t step, uint32_t row, uint32_t gv0,
                               int64_t n, uint32_t* bits, float* g, hipStream_t stream);

@@ -29,8 +29,8 @@
 //   DmaLoop     as LdsLoop, but h reaches LDS by direct buffer->LDS loads in
 //               an S-deep ring, with explicit load-count waits so that the W
 //               stream keeps its lead across chunk barriers (large batches).
-// Rows >= V and batch rows >= B read clamped (valid) addresses; their results
-// are discarded by the epilogue, so operands need no masking except for the
+// Rows outside [0, V) and batch rows >= B read clamped (valid) addresses; their
+// results are discarded by the epilogue, so operands need no masking except for the
 // k >= D tail of the stream loop.  W loads may use the non-temporal hint (NTL):
 // each W byte is read exactly once, so it should not displace h in the caches.
 #pragma once
@@ -38,6 +38,10 @@
 #include "fs_device.hpp"
 
 namespace fs {
+
+// Rows outside [0, V) (the ragged end, and the rows before 0 of a grid that
+// is shifted to align global ids) read a valid row; their results are masked.
+__device__ __forceinline__ int clamp_row(int r, int32_t V) { return min(max(r, 0), V - 1); }
 
 template <bool NTL = false>
 __device__ __forceinline__ bf16x8 load_frag(const __bf16* p) {
@@ -80,7 +84,7 @@ struct FragPtrs {
     const int lane = threadIdx.x & (kWave - 1);
     const int li = lane & 15, kb = lane >> 4;
     static_for<MR>([&](auto m) FS_INLINE {
-      a[m] = W + static_cast<size_t>(min(row0 + m * 16 + li, V - 1)) * D + kbeg + 8 * kb;
+      a[m] = W + static_cast<size_t>(clamp_row(row0 + m * 16 + li, V)) * D + kbeg + 8 * kb;
     });
     static_for<NT>([&](auto n) FS_INLINE {
       b[n] = h + static_cast<size_t>(min(col0 + n * 16 + li, B - 1)) * D + kbeg + 8 * kb;
@@ -300,7 +304,7 @@ struct LdsLoop {
     __bf16* hs = static_cast<__bf16*>(smem);
     const __bf16* arow[MR];
     static_for<MR>([&](auto m) FS_INLINE {
-      arow[m] = W + static_cast<size_t>(min(row0 + m * 16 + li, V - 1)) * D + 8 * kb;
+      arow[m] = W + static_cast<size_t>(clamp_row(row0 + m * 16 + li, V)) * D + 8 * kb;
     });
     zero_acc(acc);
 
@@ -378,9 +382,9 @@ struct LdsLoop {
 template <int MR_, int NT_, int NW_, int KC, int P, int S, int BR, int G = 1>
 struct DmaLoop {
   static constexpr int MR = MR_, NT = NT_, NW = NW_;
-  // registers to spare: the epilogue's per-row temperatures are loaded
-  // before the main loop, hiding their latency entirely
-  static constexpr bool kEarlyTemperature = true;
+  // the epilogue's per-row temperatures are loaded after the main loop
+  // (loaded before it they would hold registers the loop needs)
+  static constexpr bool kEarlyTemperature = false;
   static constexpr int kRowsPerBlock = MR * 16 * NW;
   static constexpr int kBlockCols = NT * 16;
   static constexpr int KS = KC / 32;                 // MFMA k-steps per chunk
@@ -483,7 +487,7 @@ struct DmaLoop {
     __bf16* hs = static_cast<__bf16*>(smem);
     const __bf16* arow[MR];
     static_for<MR>([&](auto m) FS_INLINE {
-      arow[m] = W + static_cast<size_t>(min(row0 + m * 16 + li, V - 1)) * D + 8 * kb;
+      arow[m] = W + static_cast<size_t>(clamp_row(row0 + m * 16 + li, V)) * D + 8 * kb;
     });
     zero_acc(acc);
 

@@ -1,0 +1,390 @@
+// fs_sampler.hpp -- the fused LM-head + Gumbel-Max sampler kernels and the
+// host-side launchers of their configurations.
+//
+// FlashSampling (wiki summary, "Method"; arXiv abstract): compute each
+// vocabulary tile's logits on chip, scale by 1/T, add per-element Gumbel
+// noise, keep one (max, argmax) pair per row and per tile, and finish with a
+// small reduction over tiles.  Because the argmax of logits plus noise
+// decomposes over any partition of the vocabulary ("Key claims"), the result
+// equals one global argmax over the full noise field.  With LSE the kernels
+// also emit each tile's log-sum-exp of the scaled logits, for the grouped
+// (hierarchical) sampler.
+//
+// Grid: x = vocabulary blocks of Loop::kRowsPerBlock rows, y = batch blocks of
+// NT * 16 rows.  The main loop (fs_mma.hpp) is a policy that leaves each
+// wave with MFMA accumulators for MR * 16 vocabulary rows x NT * 16 batch
+// rows; the epilogue runs in registers on those accumulators and the block
+// writes one (max, argmax) partial per batch row to part_[val|idx][b][block].
+//
+// The configurations are instantiated in several translation units
+// (fs_configs_*.hip) so that they compile in parallel.
+#pragma once
+
+#include "fs_internal.hpp"
+#include "fs_mma.hpp"
+
+namespace fs {
+
+template <class Loop, bool LSE>
+__global__ __launch_bounds__(Loop::NW * kWave)
+__attribute__((amdgpu_waves_per_eu(Loop::kWavesPerSimd))) void fused_sample_kernel(SampleArgs a) {
+  constexpr int MR = Loop::MR, NT = Loop::NT, NW = Loop::NW;
+  extern __shared__ __attribute__((aligned(16))) unsigned char dyn_smem[];
+  const int lane = threadIdx.x & (kWave - 1);
+  const int wave = threadIdx.x >> 6;
+  const int li = lane & 15, kb = lane >> 4;
+  // The vocabulary grid starts vocab_offset mod 4 rows before row 0, so that
+  // every lane's four consecutive rows begin at a global id divisible by 4.
+  const int shift = a.vocab_offset & 3;
+  const int row0 = Loop::row0(blockIdx.x, wave) - shift;
+  const int block_col0 = blockIdx.y * Loop::kBlockCols;
+
+  const int col0 = block_col0 + Loop::col_off(wave);  // this wave's first batch row
+  // The temperatures of the wave's batch rows are loaded all at once, before
+  // the main loop where the loop leaves registers for them, else right after
+  // it: loaded next to their uses, each batch tile would wait one full memory
+  // latency of a busy HBM.
+  float temp[NT];
+  auto load_temperatures = [&]() FS_INLINE {
+    static_for<NT>([&](auto n) FS_INLINE {
+      temp[n] = a.temperature[min(col0 + static_cast<int>(n) * 16 + li, a.B - 1)];
+    });
+  };
+  if constexpr (Loop::kEarlyTemperature) load_temperatures();
+
+  f32x4 acc[MR][NT];
+  Loop::run(a.W, a.h, a.B, a.D, a.V, row0, block_col0, acc, dyn_smem);
+  if constexpr (!Loop::kEarlyTemperature) load_temperatures();
+
+  // ---- epilogue: scale, perturb, running (max, argmax) per batch row ----
+  // Lane (li, kb) holds batch row col0 + 16n + li and vocabulary rows
+  // row0 + 16m + 4kb + r, r = 0..3: one Philox block when vocab_offset % 4 == 0.
+  // With a log-sum-exp output (grouped sampler) the same pass also keeps a
+  // running log-sum-exp of the scaled logits per batch row.
+  const Philox philox(a.seed);
+  ArgMax best[NT];
+  LseAcc lacc[NT];
+  {
+    static_for<NT>([&](auto n) FS_INLINE {
+      best[n].init();
+      if (LSE) lacc[n].init();
+      // rows b >= B run on a clamped temperature; their results are not written
+      const int b = col0 + n * 16 + li;
+      const float T = temp[n];
+      const bool greedy = row_is_greedy(T);
+      const float inv_t = row_inv_temperature(T);
+      static_for<MR>([&](auto m) FS_INLINE {
+        if (Loop::owns(wave, m, n)) {
+          const int v0 = row0 + m * 16 + 4 * kb;  // vocab_offset + v0 is a multiple of 4
+          push_four<LSE>(best[n], acc[m][n], v0, a.V,
+                                 static_cast<uint32_t>(a.vocab_offset + v0),
+                                 static_cast<uint32_t>(b), a.step, greedy, inv_t, philox,
+                                 &lacc[n]);
+        }
+      });
+    });
+    // lanes l, l^16, l^32, l^48 hold the same batch row
+    static_for<NT>([&](auto n) FS_INLINE {
+      best[n].xor_reduce(16);
+      best[n].xor_reduce(32);
+      if (LSE) {
+        lacc[n].xor_reduce(16);
+        lacc[n].xor_reduce(32);
+      }
+    });
+  }
+
+  __shared__ float s_val[NW][NT * 16];
+  __shared__ int32_t s_idx[NW][NT * 16];
+  if (kb == 0) {
+    static_for<NT>([&](auto n) FS_INLINE {
+      s_val[wave][n * 16 + li] = best[n].v;
+      s_idx[wave][n * 16 + li] = best[n].i;
+    });
+  }
+  __syncthreads();
+  // block column c is covered by the waves w with col_off(w) == c - c % (NT*16)
+  for (int c = threadIdx.x; c < Loop::kBlockCols; c += NW * kWave) {
+    const int b = block_col0 + c;
+    if (b >= a.B) break;
+    ArgMax m;
+    m.init();
+#pragma unroll
+    for (int w = 0; w < NW; ++w)
+      if (Loop::col_off(w) == c - c % (NT * 16)) m.push(s_val[w][c % (NT * 16)], s_idx[w][c % (NT * 16)]);
+    const size_t o = static_cast<size_t>(b) * a.S + blockIdx.x;
+    a.part_val[o] = m.v;
+    a.part_idx[o] = m.i;
+  }
+  if constexpr (LSE) {  // the same two arrays carry the (m, s) pairs
+    __syncthreads();
+    if (kb == 0) {
+      static_for<NT>([&](auto n) FS_INLINE {
+        s_val[wave][n * 16 + li] = lacc[n].m;
+        s_idx[wave][n * 16 + li] = __float_as_int(lacc[n].s);
+      });
+    }
+    __syncthreads();
+    for (int c = threadIdx.x; c < Loop::kBlockCols; c += NW * kWave) {
+      const int b = block_col0 + c;
+      if (b >= a.B) break;
+      LseAcc l;
+      l.init();
+#pragma unroll
+      for (int w = 0; w < NW; ++w)
+        if (Loop::col_off(w) == c - c % (NT * 16))
+          l.merge(s_val[w][c % (NT * 16)], __int_as_float(s_idx[w][c % (NT * 16)]));
+      a.part_lse[static_cast<size_t>(b) * a.S + blockIdx.x] = l.value(row_is_greedy(a.temperature[b]));
+    }
+  }
+}
+
+// ---------------------------------------------------------------------------
+// Persistent K-split sampler for small batches (NT * 16 batch rows).
+//
+// Block = NW waves, one or two per SIMD, launched once per CU slot.  Wave w
+// owns the D-slice [w*KS*32, (w+1)*KS*32) and keeps h for that slice in
+// registers for the whole kernel, so h is read from memory once per block.
+// Blocks sweep the 16-row vocabulary groups g = block, block + G, ...: the
+// groups being streamed at any moment form a narrow moving window of W,
+// which keeps HBM row-buffer locality high.  W fragments stream through a
+// P-deep register ring that runs ahead across group boundaries.  After each
+// group the NW partial accumulators are summed through LDS (two buffers,
+// fixed wave order) by one owner wave per batch tile, which runs the
+// epilogue; ownership rotates over the waves.  The running (max, argmax)
+// persists across groups, so a block emits one partial per batch row.
+// Requires D == 32 * NW * KS.
+// ---------------------------------------------------------------------------
+template <int NT, int NW, int KS, int P, bool LSE>
+__global__ __launch_bounds__(NW * kWave) void persist_sample_kernel(SampleArgs a) {
+  static_assert(KS % P == 0, "the load ring must tile a group");
+  extern __shared__ __attribute__((aligned(16))) unsigned char dyn_smem[];
+  f32x4* red = reinterpret_cast<f32x4*>(dyn_smem);  // [2][NW][NT][kWave]
+  const int lane = threadIdx.x & (kWave - 1);
+  const int wave = threadIdx.x >> 6;
+  const int li = lane & 15, kb = lane >> 4;
+  const int D = a.D;
+  const int kbeg = wave * KS * 32 + 8 * kb;
+  // 16-row groups over a vocabulary grid shifted as in the tiled kernel
+  const int shift = a.vocab_offset & 3;
+  const int ngroups = (a.V + shift + 15) / 16;
+  const int G = gridDim.x;
+
+  bf16x8 hreg[KS][NT];
+  bool bvalid[NT], greedy[NT];
+  float inv_t[NT];
+  static_for<NT>([&](auto n) FS_INLINE {
+    const int b = n * 16 + li;
+    bvalid[n] = b < a.B;
+    const __bf16* hp = a.h + static_cast<size_t>(min(b, a.B - 1)) * D + kbeg;
+    static_for<KS>([&](auto s) FS_INLINE { hreg[s][n] = load_frag(hp + s * 32); });
+    const float T = bvalid[n] ? a.temperature[b] : 1.0f;
+    greedy[n] = row_is_greedy(T);
+    inv_t[n] = row_inv_temperature(T);
+  });
+
+  auto group_ptr = [&](int g) FS_INLINE {
+    return a.W + static_cast<size_t>(clamp_row(min(g, ngroups - 1) * 16 + li - shift, a.V)) * D + kbeg;
+  };
+  const Philox philox(a.seed);
+  ArgMax best[NT];
+  LseAcc lacc[NT];  // grouped sampler only: running log-sum-exp per batch row
+  static_for<NT>([&](auto n) FS_INLINE {
+    best[n].init();
+    if (LSE) lacc[n].init();
+  });
+
+  int g = blockIdx.x;
+  const __bf16* ap = group_ptr(g);
+  const __bf16* ap_next = group_ptr(g + G);
+  bf16x8 ring[P];
+  static_for<P>([&](auto p) FS_INLINE { ring[p] = load_frag(ap + p * 32); });
+
+  for (int it = 0; g < ngroups; g += G, ++it) {
+    f32x4 acc[NT];
+    static_for<NT>([&](auto n) FS_INLINE { acc[n] = f32x4{0.f, 0.f, 0.f, 0.f}; });
+    static_for<KS>([&](auto sc) FS_INLINE {
+      constexpr int s = decltype(sc)::value;
+      constexpr int slot = s % P;
+      static_for<NT>([&](auto n) FS_INLINE { acc[n] = mfma16(ring[slot], hreg[s][n], acc[n]); });
+      // refill with the k-step P ahead (the next group's, past the end of this one)
+      if constexpr (s + P < KS)
+        ring[slot] = load_frag(ap + (s + P) * 32);
+      else
+        ring[slot] = load_frag(ap_next + (s + P - KS) * 32);
+    });
+    ap = ap_next;
+    ap_next = group_ptr(g + 2 * G);
+
+    const int par = it & 1;
+    static_for<NT>([&](auto n) FS_INLINE {
+      red[((par * NW + wave) * NT + n) * kWave + lane] = acc[n];
+    });
+    __syncthreads();
+    static_for<NT>([&](auto n) FS_INLINE {
+      if ((n + it) % NW == wave && bvalid[n]) {
+        f32x4 z = red[((par * NW + 0) * NT + n) * kWave + lane];
+        for (int w = 1; w < NW; ++w) z += red[((par * NW + w) * NT + n) * kWave + lane];
+        const int b = n * 16 + li;
+        const int v0 = g * 16 + 4 * kb - shift;  // ids grow with g for each owner
+        const uint32_t gv0 = static_cast<uint32_t>(a.vocab_offset + v0);
+        push_four<LSE>(best[n], z, v0, a.V, gv0, static_cast<uint32_t>(b), a.step,
+                               greedy[n], inv_t[n], philox, &lacc[n]);
+      }
+    });
+  }
+
+  static_for<NT>([&](auto n) FS_INLINE {
+    best[n].xor_reduce(16);
+    best[n].xor_reduce(32);
+    if (LSE) {
+      lacc[n].xor_reduce(16);
+      lacc[n].xor_reduce(32);
+    }
+  });
+  __shared__ float s_val[NW][NT * 16];
+  __shared__ int32_t s_idx[NW][NT * 16];
+  if (kb == 0) {
+    static_for<NT>([&](auto n) FS_INLINE {
+      s_val[wave][n * 16 + li] = best[n].v;
+      s_idx[wave][n * 16 + li] = best[n].i;
+    });
+  }
+  __syncthreads();
+  for (int c = threadIdx.x; c < NT * 16 && c < a.B; c += NW * kWave) {
+    ArgMax m;
+    m.init();
+#pragma unroll
+    for (int w = 0; w < NW; ++w) m.push(s_val[w][c], s_idx[w][c]);
+    const size_t o = static_cast<size_t>(c) * a.S + blockIdx.x;
+    a.part_val[o] = m.v;
+    a.part_idx[o] = m.i;
+  }
+  if constexpr (LSE) {  // the same two arrays carry the (m, s) pairs
+    __syncthreads();
+    if (kb == 0) {
+      static_for<NT>([&](auto n) FS_INLINE {
+        s_val[wave][n * 16 + li] = lacc[n].m;
+        s_idx[wave][n * 16 + li] = __float_as_int(lacc[n].s);
+      });
+    }
+    __syncthreads();
+    for (int c = threadIdx.x; c < NT * 16 && c < a.B; c += NW * kWave) {
+      LseAcc l;
+      l.init();
+#pragma unroll
+      for (int w = 0; w < NW; ++w) l.merge(s_val[w][c], __int_as_float(s_idx[w][c]));
+      a.part_lse[static_cast<size_t>(c) * a.S + blockIdx.x] = l.value(row_is_greedy(a.temperature[c]));
+    }
+  }
+}
+
+// ---------------------------------------------------------------------------
+// Host side: launchers and the configuration entries built from them.
+// ---------------------------------------------------------------------------
+
+// Raises the dynamic-LDS limit of a kernel once (it may exceed the default).
+template <class Kernel>
+hipError_t allow_smem(Kernel kernel, size_t smem) {
+  return hipFuncSetAttribute(reinterpret_cast<const void*>(kernel),
+                             hipFuncAttributeMaxDynamicSharedMemorySize, static_cast<int>(smem));
+}
+
+template <class Loop>
+hipError_t launch_cfg(SampleArgs& a, hipStream_t stream) {
+  constexpr int rows = Loop::kRowsPerBlock;
+  static_assert(rows >= kMinRowsPerBlock, "split count bound");
+  if (!Loop::supports(a.D) || static_cast<size_t>(a.B) * a.D * 2 > Loop::kMaxHBytes)
+    return hipErrorInvalidValue;
+  constexpr size_t smem = Loop::kSmemBytes;
+  if (smem > 0) {
+    static const hipError_t attr = [] {
+      const hipError_t e = allow_smem(&fused_sample_kernel<Loop, false>, smem);
+      return e != hipSuccess ? e : allow_smem(&fused_sample_kernel<Loop, true>, smem);
+    }();
+    if (attr != hipSuccess) return attr;
+  }
+  a.S = (a.V + (a.vocab_offset & 3) + rows - 1) / rows;
+  const dim3 grid(a.S, (a.B + Loop::kBlockCols - 1) / Loop::kBlockCols);
+  const dim3 block(Loop::NW * kWave);
+  if (a.part_lse == nullptr)
+    fused_sample_kernel<Loop, false><<<grid, block, smem, stream>>>(a);
+  else
+    fused_sample_kernel<Loop, true><<<grid, block, smem, stream>>>(a);
+  return hipGetLastError();
+}
+
+template <class Loop>
+bool supports_cfg(int32_t B, int32_t D) {
+  return Loop::supports(D) && static_cast<size_t>(B) * D * 2 <= Loop::kMaxHBytes;
+}
+
+// Blocks of `kernel` that fit on one CU, times the CU count of the current
+// device (cached per device).
+template <class Kernel>
+int resident_blocks(Kernel kernel, int threads, size_t smem) {
+  static int cached_dev = -1, cached = 0;
+  int dev = 0;
+  if (hipGetDevice(&dev) != hipSuccess) return 0;
+  if (dev != cached_dev) {
+    int cus = 0, per_cu = 0;
+    if (hipDeviceGetAttribute(&cus, hipDeviceAttributeMultiprocessorCount, dev) != hipSuccess ||
+        hipOccupancyMaxActiveBlocksPerMultiprocessor(&per_cu, kernel, threads, smem) !=
+            hipSuccess)
+      return 0;
+    cached = cus * (per_cu > 0 ? per_cu : 1);
+    cached_dev = dev;
+  }
+  return cached;
+}
+
+template <int NT, int NW, int KS, int P>
+struct Persist {
+  static constexpr size_t kSmemBytes = 2ull * NW * NT * kWave * sizeof(f32x4);
+  static bool supports(int32_t B, int32_t D) { return B <= NT * 16 && D == 32 * NW * KS; }
+  template <bool LSE>
+  static hipError_t go(SampleArgs& a, hipStream_t stream) {
+    const auto kernel = persist_sample_kernel<NT, NW, KS, P, LSE>;
+    const int slots = resident_blocks(kernel, NW * kWave, kSmemBytes);
+    if (slots <= 0) return hipErrorInvalidDevice;
+    const int ngroups = (a.V + (a.vocab_offset & 3) + 15) / 16;
+    a.S = ngroups < slots ? ngroups : slots;
+    kernel<<<a.S, NW * kWave, kSmemBytes, stream>>>(a);
+    return hipGetLastError();
+  }
+  static hipError_t launch(SampleArgs& a, hipStream_t stream) {
+    if (!supports(a.B, a.D)) return hipErrorInvalidValue;
+    return a.part_lse == nullptr ? go<false>(a, stream) : go<true>(a, stream);
+  }
+};
+
+template <class Loop>
+constexpr FusedConfig make_cfg(const char* name, int order) {
+  return {name, Loop::kRowsPerBlock, &launch_cfg<Loop>, &supports_cfg<Loop>, order};
+}
+
+template <class Pol>
+constexpr FusedConfig make_persist(const char* name, int order) {
+  return {name, 16, &Pol::launch, &Pol::supports, order};
+}
+
+#define FS_STREAM(MR, NT, NW, P, NTL) \
+  make_cfg<StreamLoop<MR, NT, NW, P, NTL>>("stream_mr" #MR "_nt" #NT "_nw" #NW "_p" #P "_ntl" #NTL, 0)
+#define FS_KSPLIT(MR, NT, NW, P, NTL) \
+  make_cfg<KSplitLoop<MR, NT, NW, P, NTL>>("ksplit_mr" #MR "_nt" #NT "_nw" #NW "_p" #P "_ntl" #NTL, NW)
+#define FS_LDS(MR, NT, NW, KC, P, NTL)                                                           \
+  make_cfg<LdsLoop<MR, NT, NW, KC, P, NTL>>(                                                   \
+      "lds_mr" #MR "_nt" #NT "_nw" #NW "_kc" #KC "_p" #P "_ntl" #NTL, 0)
+#define FS_LDSR(MR, NT, NW, KC, P, WB, BR)                                                     \
+  make_cfg<LdsLoop<MR, NT, NW, KC, P, false, WB, BR>>(                                         \
+      "lds_mr" #MR "_nt" #NT "_nw" #NW "_kc" #KC "_p" #P "_wb" #WB "_br" #BR, 0)
+#define FS_DMA(MR, NT, NW, KC, P, S, BR)                                                      \
+  make_cfg<DmaLoop<MR, NT, NW, KC, P, S, BR>>(                                               \
+      "dma_mr" #MR "_nt" #NT "_nw" #NW "_kc" #KC "_p" #P "_s" #S "_br" #BR, 0)
+#define FS_DMAG(MR, NT, NW, KC, P, S, BR, G)                                                  \
+  make_cfg<DmaLoop<MR, NT, NW, KC, P, S, BR, G>>(                                            \
+      "dma_mr" #MR "_nt" #NT "_nw" #NW "_kc" #KC "_p" #P "_s" #S "_br" #BR "_g" #G, 0)
+#define FS_PERSIST(NT, NW, KS, P) \
+  make_persist<Persist<NT, NW, KS, P>>("persist_nt" #NT "_nw" #NW "_ks" #KS "_p" #P, 100 + NW)
+
+}  // namespace fs
