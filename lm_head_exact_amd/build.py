@@ -24,6 +24,9 @@ FLAGS = [
     "-Wall", "-Wno-unused-result",
     # keep hipcc from forming packed fp32 instructions in device code
     "-Xclang", "-target-feature", "-Xclang", "-packed-fp32-ops",
+    # every multiply and add rounds as written (the score z * (1/T) + g is two
+    # roundings); fused multiply-adds only where the source asks for fmaf
+    "-ffp-contract=off",
     f"-I{os.path.join(ROOT, 'include')}",
 ]
 

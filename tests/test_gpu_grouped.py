@@ -112,8 +112,9 @@ def _synthetic_partials(P, B, seed):
     lse = (8.0 + 1.5 * rng.standard_normal((P, B))).astype(np.float32)
     val = (lse + rng.gumbel(size=(P, B))).astype(np.float32)
     ids = (np.arange(P)[:, None] * 1000 + rng.integers(0, 1000, size=(P, B))).astype(np.int32)
-    # ties and equal keys on some rows
-    lse[1, ::11] = lse[0, ::11]
+    # equal log-sum-exps of two groups on some rows (ties for greedy rows)
+    if P >= 2:
+        lse[1, ::11] = lse[0, ::11]
     T = np.resize(np.array([1.0, 0.7, 0.0, 1.3, -0.0, 2.0, 0.4], np.float32), B)
     return val, ids, lse, T
 
