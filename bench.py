@@ -7,7 +7,8 @@ Llama-3-8B-shaped LM head (D = 4096, V = 128256, bf16), with the inputs
 already resident in device memory and a fresh (seed, step) per step.  The
 headline line is B = 32; the same line carries the B = 1 .. 256 sweep, the
 unfused baseline (logits and probabilities through device memory) timed the
-same way, the fused kernel's roofline fraction and the CPU oracle's rate.
+same way, the grouped (hierarchical) sampler over 1 and 8 vocabulary groups,
+the fused kernel's roofline fraction and the CPU oracle's rate.
 
 Prints ONE JSON line on stdout.  Usage:
   python bench.py [--gpus 1] [--steps K] [--warmup W] [--batch 32]
@@ -40,6 +41,7 @@ def parse():
     ap.add_argument("--sweep-steps", type=int, default=100)
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--no-unfused", action="store_true")
+    ap.add_argument("--no-grouped", action="store_true")
     ap.add_argument("--profile-pass", action="store_true")
     return ap.parse_args()
 
@@ -206,6 +208,45 @@ def main():
             del ukp
         sweep.append(entry)
         del kp
+    # Grouped (hierarchical) sampler: the vocabulary as G contiguous groups,
+    # one fs_sample_partial_lse per group into its slot, then fs_merge_lse.
+    grouped = []
+    for b, G in ((B, 1), (B, 8), (256, 1), (256, 8)):
+        if args.no_grouped or G < 1 or V % G:
+            continue
+        h_g = wl.make_h(wlk, b, dev)
+        T_g = wl.make_temperature(wlk, b, dev)
+        pv = torch.empty(G, b, dtype=torch.float32, device=dev)
+        pi = torch.empty(G, b, dtype=torch.int32, device=dev)
+        pl = torch.empty(G, b, dtype=torch.float32, device=dev)
+        ws = fsl.alloc_workspace(fsl.workspace_bytes(b, D, V // G), dev)
+        outs = (torch.empty(b, dtype=torch.int32, device=dev),
+                torch.empty(b, dtype=torch.float32, device=dev),
+                torch.empty(b, dtype=torch.float32, device=dev))
+        Vg = V // G
+
+        def gfn(i, h_g=h_g, T_g=T_g, pv=pv, pi=pi, pl=pl, ws=ws, outs=outs, G=G, Vg=Vg):
+            seed, step = wlk.sampler_seed(i)
+            for p in range(G):
+                fsl.sample_partial_lse(h_g, W[p * Vg:(p + 1) * Vg], T_g, seed, step, p * Vg,
+                                       pv[p], pi[p], pl[p], workspace=ws)
+            fsl.merge_lse(pv, pi, pl, T_g, seed, step, out=outs)
+        # one step is G + 1 small launches: replay it as a captured graph so that
+        # host-side call overhead does not stand in for device time
+        for i in range(3):
+            gfn(i)
+        torch.cuda.synchronize()
+        graph = torch.cuda.CUDAGraph()
+        with torch.cuda.graph(graph):
+            gfn(7)
+        gt = time_steps(torch, lambda i: graph.replay(), max(10, args.sweep_steps // 2), 5,
+                        torch.cuda.current_stream(dev)) * 1e3
+        del graph
+        plain = next((e["us_per_step"] for e in sweep if e["B"] == b), None)
+        grouped.append({"B": b, "groups": G, "us_per_step": round(gt, 2),
+                        "fs_sample_us_per_step": plain})
+        del h_g, T_g, pv, pi, pl, ws, outs
+
     unf_us = None
     if not args.no_unfused:
         uf, ukp = make_step(B, unfused=True)
@@ -247,6 +288,7 @@ def main():
         "unfused_us_per_step": round(unf_us, 2) if unf_us is not None else None,
         "cpu_baseline": cpu,
         "sweep": sweep,
+        "grouped_lse": grouped,
         "device": {"name": props.name, "cus": props.multi_processor_count,
                    "gcn_arch": getattr(props, "gcnArchName", "")},
     }
