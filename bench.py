@@ -8,7 +8,8 @@ already resident in device memory and a fresh (seed, step) per step.  The
 headline line is B = 32; the same line carries the B = 1 .. 256 sweep, the
 unfused baseline (logits and probabilities through device memory) timed the
 same way, the grouped (hierarchical) sampler over 1 and 8 vocabulary groups,
-the fused kernel's roofline fraction and the CPU oracle's rate.
+the Qwen3-shaped, large-batch and vocabulary-shard heads, the fused kernel's
+roofline fraction and the CPU oracle's rate.
 
 Prints ONE JSON line on stdout.  Usage:
   python bench.py [--gpus 1] [--steps K] [--warmup W] [--batch 32]
@@ -42,6 +43,7 @@ def parse():
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--no-unfused", action="store_true")
     ap.add_argument("--no-grouped", action="store_true")
+    ap.add_argument("--no-workloads", action="store_true")
     ap.add_argument("--profile-pass", action="store_true")
     return ap.parse_args()
 
@@ -247,6 +249,47 @@ def main():
                         "fs_sample_us_per_step": plain})
         del h_g, T_g, pv, pi, pl, ws, outs
 
+    # The other LM-head shapes (fused step only): Qwen3-shaped (D=5120,
+    # V=151936, mixed temperatures with greedy rows), large batch (D=8192) and
+    # one GPU's share of an 8-way vocabulary shard (D=8192, V=16032 at
+    # vocab_offset 48096).  The shard's W (263 MB) would stay in the 256 MB
+    # last-level cache between steps, so its steps rotate over four copies
+    # (1.05 GB, "cold"); the same-copy rate is reported beside it ("hot").
+    workloads = []
+    if not args.no_workloads:
+        del_keep = None
+        for wk, Bs, copies in ((wl.QWEN3, (64, 128, 256), 1), (wl.LARGE_BATCH, (256, 512), 1),
+                               (wl.TP8_SHARD, (1, 64, 256), 4)):
+            Ws = [wl.make_w(wk, dev) for _ in range(copies)]
+            for b in Bs:
+                h_w = wl.make_h(wk, b, dev)
+                T_w = wl.make_temperature(wk, b, dev)
+                out_w = (torch.empty(b, dtype=torch.int32, device=dev),
+                         torch.empty(b, dtype=torch.float32, device=dev))
+                ws_w = fsl.alloc_workspace(fsl.workspace_bytes(b, wk.D, wk.V), dev)
+
+                def wfn(i, Ws=Ws, h_w=h_w, T_w=T_w, out_w=out_w, ws_w=ws_w, wk=wk, rot=True):
+                    seed, step = wk.sampler_seed(i)
+                    fsl.sample(h_w, Ws[i % len(Ws) if rot else 0], T_w, seed, step,
+                               vocab_offset=wk.vocab_offset, out=out_w, workspace=ws_w)
+                t = time_steps(torch, wfn, max(20, args.sweep_steps // 2), 5, stream) * 1e3
+                roof = max(2 * wk.V * wk.D / (HBM_PEAK_GBS * 1e3),
+                           flops(b, wk.D, wk.V) / (MFMA_BF16_PEAK_TFLOPS * 1e6))
+                e = {"workload": wk.name, "B": b, "D": wk.D, "V": wk.V,
+                     "vocab_offset": wk.vocab_offset,
+                     "config": fsl.config_name(fsl.selected_config(b, wk.D, wk.V)),
+                     "us_per_step": round(t, 2), "roofline_us": round(roof, 2),
+                     "frac_of_roofline": round(roof / t, 4)}
+                if copies > 1:
+                    th = time_steps(torch, lambda i: wfn(i, rot=False), max(20, args.sweep_steps // 2),
+                                    5, stream) * 1e3
+                    e["w_copies_rotated"] = copies
+                    e["hot_us_per_step"] = round(th, 2)
+                workloads.append(e)
+                del h_w, T_w, out_w, ws_w
+            del Ws
+            torch.cuda.empty_cache()
+
     unf_us = None
     if not args.no_unfused:
         uf, ukp = make_step(B, unfused=True)
@@ -289,6 +332,7 @@ def main():
         "cpu_baseline": cpu,
         "sweep": sweep,
         "grouped_lse": grouped,
+        "other_workloads": workloads,
         "device": {"name": props.name, "cus": props.multi_processor_count,
                    "gcn_arch": getattr(props, "gcnArchName", "")},
     }
