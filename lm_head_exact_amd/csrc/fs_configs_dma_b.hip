@@ -10,6 +10,9 @@ int fused_configs_dma_b(const FusedConfig** out) {
       FS_DMA(4, 8, 8, 64, 4, 3, 4),
       FS_DMAG(2, 16, 8, 64, 8, 3, 4, 2),
       FS_DMAG(2, 8, 8, 64, 4, 4, 4, 2),
+      FS_DMAR(2, 16, 8, 64, 4, 4, 4, 2),
+      FS_DMAR(4, 8, 8, 64, 4, 3, 4, 2),
+      FS_DMAR(4, 4, 8, 64, 4, 3, 4, 2),
   };
   *out = k;
   return static_cast<int>(sizeof(k) / sizeof(k[0]));

@@ -379,7 +379,7 @@ struct LdsLoop {
 // the W stream keeps its P-step lead across chunk boundaries.
 // Requires D % (KC * U) == 0.
 // ---------------------------------------------------------------------------
-template <int MR_, int NT_, int NW_, int KC, int P, int S, int BR, int G = 1>
+template <int MR_, int NT_, int NW_, int KC, int P, int S, int BR, int G = 1, bool ROT = false>
 struct DmaLoop {
   static constexpr int MR = MR_, NT = NT_, NW = NW_;
   // the epilogue's per-row temperatures are loaded after the main loop
@@ -494,10 +494,16 @@ struct DmaLoop {
     // Every load is issued unconditionally (indices past the end are clamped
     // and their data never used), so the per-chunk load counts are constants.
     const int nch = D / KC, nks = D / 32;
-    static_for<S - 1>([&](auto s) FS_INLINE { stage(h, B, D, col0, min(static_cast<int>(s), nch - 1), hs + s * STAGE); });
+    // ROT: each block runs its chunks in a rotated order, starting at a
+    // block-dependent chunk, so that the blocks' concurrent W reads fall on
+    // different offsets of their rows (the rows are a power of two apart).
+    const int r0 = ROT ? static_cast<int>((blockIdx.x * 37u) % static_cast<unsigned>(nch)) : 0;
+    auto rc = [&](int c) FS_INLINE { const int x = c + r0; return x >= nch ? x - nch : x; };
+    auto rq = [&](int q) FS_INLINE { const int x = q + r0 * KS; return x >= nks ? x - nks : x; };
+    static_for<S - 1>([&](auto s) FS_INLINE { stage(h, B, D, col0, rc(min(static_cast<int>(s), nch - 1)), hs + s * STAGE); });
     bf16x8 ring[P][MR];
     static_for<P>([&](auto p) FS_INLINE {
-      const int q = min(static_cast<int>(p), nks - 1);
+      const int q = rq(min(static_cast<int>(p), nks - 1));
       static_for<MR>([&](auto m) FS_INLINE { ring[p][m] = load_frag(arow[m] + q * 32); });
     });
     wait_vm<(S - 2) * IPW + P * MR>();  // chunk 0 staged
@@ -508,7 +514,7 @@ struct DmaLoop {
       static_for<U>([&](auto u) FS_INLINE {
         const int c = c0 + u;
         const int slot_n = slot_c == 0 ? S - 1 : slot_c - 1;  // slot of chunk c + S - 1
-        stage(h, B, D, col0, min(c + S - 1, nch - 1), hs + slot_n * STAGE);
+        stage(h, B, D, col0, rc(min(c + S - 1, nch - 1)), hs + slot_n * STAGE);
         __builtin_amdgcn_sched_barrier(0);
         const __bf16* buf = hs + slot_c * STAGE;
         constexpr int T = KS * NT;
@@ -526,7 +532,7 @@ struct DmaLoop {
           if constexpr (n == NT - 1 && (g + 1) % G == 0) {
             static_for<G>([&](auto j) FS_INLINE {
               constexpr int sl = (g + 1 - G + decltype(j)::value) % P;
-              const int q = min(c * KS + s + 1 - G + decltype(j)::value + P, nks - 1);
+              const int q = rq(min(c * KS + s + 1 - G + decltype(j)::value + P, nks - 1));
               static_for<MR>([&](auto m) FS_INLINE { ring[sl][m] = load_frag(arow[m] + q * 32); });
             });
           }

@@ -384,6 +384,9 @@ constexpr FusedConfig make_persist(const char* name, int order) {
 #define FS_DMAG(MR, NT, NW, KC, P, S, BR, G)                                                  \
   make_cfg<DmaLoop<MR, NT, NW, KC, P, S, BR, G>>(                                            \
       "dma_mr" #MR "_nt" #NT "_nw" #NW "_kc" #KC "_p" #P "_s" #S "_br" #BR "_g" #G, 0)
+#define FS_DMAR(MR, NT, NW, KC, P, S, BR, G)                                                  \
+  make_cfg<DmaLoop<MR, NT, NW, KC, P, S, BR, G, true>>(                                      \
+      "dmarot_mr" #MR "_nt" #NT "_nw" #NW "_kc" #KC "_p" #P "_s" #S "_br" #BR "_g" #G, 0)
 #define FS_PERSIST(NT, NW, KS, P) \
   make_persist<Persist<NT, NW, KS, P>>("persist_nt" #NT "_nw" #NW "_ks" #KS "_p" #P, 100 + NW)
 

@@ -61,7 +61,7 @@ def _num_configs():
     try:
         return fsl.num_configs()
     except Exception:  # library not built: collection must still succeed
-        return 26
+        return 29
 
 
 @pytest.mark.parametrize("cfg", range(_num_configs()))
@@ -145,6 +145,11 @@ def _order_class(name):
     order)."""
     if name.startswith(("ksplit", "persist")):
         return "kslices_" + name.split("_nw")[1].split("_")[0]
+    if name.startswith("dmarot"):
+        # k chunks in an order rotated by the block index: equal for equal
+        # block height (16 * MR * NW rows) and chunk width
+        f = dict(t[:2] == "kc" and ("kc", t[2:]) or (t[:2], t[2:]) for t in name.split("_")[1:])
+        return f"rotated_rows{16 * int(f['mr']) * int(f['nw'])}_kc{f['kc']}"
     return "whole_k"
 
 
