@@ -500,12 +500,18 @@ struct DmaLoop {
     const int r0 = ROT ? static_cast<int>((blockIdx.x * 37u) % static_cast<unsigned>(nch)) : 0;
     auto rc = [&](int c) FS_INLINE { const int x = c + r0; return x >= nch ? x - nch : x; };
     auto rq = [&](int q) FS_INLINE { const int x = q + r0 * KS; return x >= nks ? x - nks : x; };
-    static_for<S - 1>([&](auto s) FS_INLINE { stage(h, B, D, col0, rc(min(static_cast<int>(s), nch - 1)), hs + s * STAGE); });
+    // The waits below count loads by issue order, so the prologue's groups are
+    // fenced: staging of chunks 0 .. S-2 in order, then the W ring.
+    static_for<S - 1>([&](auto s) FS_INLINE {
+      stage(h, B, D, col0, rc(min(static_cast<int>(s), nch - 1)), hs + s * STAGE);
+      __builtin_amdgcn_sched_barrier(0);
+    });
     bf16x8 ring[P][MR];
     static_for<P>([&](auto p) FS_INLINE {
       const int q = rq(min(static_cast<int>(p), nks - 1));
       static_for<MR>([&](auto m) FS_INLINE { ring[p][m] = load_frag(arow[m] + q * 32); });
     });
+    __builtin_amdgcn_sched_barrier(0);
     wait_vm<(S - 2) * IPW + P * MR>();  // chunk 0 staged
     barrier();
 
