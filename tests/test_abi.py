@@ -104,3 +104,56 @@ def test_configs(L):
     assert L.fs_force_config(-1) == bd.FS_OK
     assert L.fs_selected_config(1, 4096, 128256) == auto[0]
     assert L.fs_selected_config(1, 7, 10) == -1
+
+
+def _sample_lse(L, h=ALIGNED, W=ALIGNED, B=4, D=256, V=1000, off=0, T=ALIGNED, val=ALIGNED,
+                ids=ALIGNED, lse=ALIGNED, ws=WS_ALIGNED, wsb=1 << 30):
+    return L.fs_sample_partial_lse(h, W, B, D, V, off, T, 1, 2, val, ids, lse, ws, wsb, None)
+
+
+@pytest.mark.parametrize("kw,status", [
+    (dict(D=7), bd.FS_ERR_INVALID_ARG),
+    (dict(V=0), bd.FS_ERR_INVALID_ARG),
+    (dict(B=-1), bd.FS_ERR_INVALID_ARG),
+    (dict(off=-5), bd.FS_ERR_INVALID_ARG),
+    (dict(h=None), bd.FS_ERR_INVALID_ARG),
+    (dict(lse=None), bd.FS_ERR_INVALID_ARG),
+    (dict(lse=ALIGNED + 2), bd.FS_ERR_INVALID_ARG),
+    (dict(ids=ALIGNED + 1), bd.FS_ERR_INVALID_ARG),
+    (dict(W=ALIGNED + 8), bd.FS_ERR_INVALID_ARG),
+    (dict(wsb=16), bd.FS_ERR_WORKSPACE),
+    (dict(B=0, h=None, W=None, T=None, ids=None, val=None, lse=None, ws=None), bd.FS_OK),
+])
+def test_sample_partial_lse_argument_errors(L, kw, status):
+    assert _sample_lse(L, **kw) == status
+    if status != bd.FS_OK:
+        assert len(L.fs_last_error()) > 0
+
+
+def _merge_lse(L, val=ALIGNED, ids=ALIGNED, lse=ALIGNED, P=2, B=4, T=ALIGNED, out_ids=ALIGNED,
+               out_val=ALIGNED, out_lse=ALIGNED):
+    return L.fs_merge_lse(val, ids, lse, P, B, T, 1, 2, out_ids, out_val, out_lse, None)
+
+
+@pytest.mark.parametrize("kw,status", [
+    (dict(P=0), bd.FS_ERR_INVALID_ARG),
+    (dict(B=-1), bd.FS_ERR_INVALID_ARG),
+    (dict(lse=None), bd.FS_ERR_INVALID_ARG),
+    (dict(T=None), bd.FS_ERR_INVALID_ARG),
+    (dict(out_lse=None), bd.FS_ERR_INVALID_ARG),
+    (dict(val=ALIGNED + 2), bd.FS_ERR_INVALID_ARG),
+    (dict(out_lse=ALIGNED + 1), bd.FS_ERR_INVALID_ARG),
+    (dict(P=1 << 20, B=1 << 21), bd.FS_ERR_INVALID_ARG),
+    (dict(B=0, val=None, ids=None, lse=None, T=None, out_ids=None, out_val=None, out_lse=None),
+     bd.FS_OK),
+])
+def test_merge_lse_argument_errors(L, kw, status):
+    assert _merge_lse(L, **kw) == status
+
+
+def test_workspace_covers_the_shifted_grid(L):
+    """Unaligned vocabulary offsets shift the tile grid by up to 3 rows, which
+    can add one block of 16 rows: the workspace is sized for it."""
+    for V in (13, 16, 17, 1000, 16032):
+        ws = L.fs_workspace_bytes(5, 256, V)
+        assert ws >= 3 * 4 * 5 * ((V + 3 + 15) // 16)
