@@ -65,23 +65,25 @@ TRAFFIC_PROFILE = os.path.join(ROOT, "profiles", "fused_sample_llama3_b32_hbm_tr
 def kernel_sources_sha256():
     """Fingerprint of the sources the fused sampler kernels are compiled
     from: counters taken on other sources no longer describe the kernel that
-    runs.  (The unfused baseline and the host-side API live in other files.)"""
+    runs.  (Which configuration runs is checked by name, beside it; the
+    configuration table, the merges, the unfused baseline and the host-side
+    API live in other files.)"""
     import hashlib
     csrc = os.path.join(ROOT, "lm_head_exact_amd", "csrc")
     h = hashlib.sha256()
     for name in ("fs_device.hpp", "fs_internal.hpp", "fs_mma.hpp", "fs_sampler.hpp",
-                 "fs_fused.hip", "fs_configs_small.hip", "fs_configs_lds.hip",
+                 "fs_configs_small.hip", "fs_configs_lds.hip",
                  "fs_configs_dma_a.hip", "fs_configs_dma_b.hip"):
         h.update(name.encode())
         h.update(open(os.path.join(csrc, name), "rb").read())
     return h.hexdigest()
 
 
-def measured_traffic(B):
+def measured_traffic(B, config):
     """HBM bytes per launch of the fused kernel (read + written) from the
     committed rocprofv3 FETCH_SIZE / WRITE_SIZE summary, calibrated against a
-    copy of known size; None when absent, taken at another batch size, or
-    taken on different kernel sources."""
+    copy of known size; None when absent, taken at another batch size, on
+    another configuration or on different kernel sources."""
     try:
         kv = {}
         for line in open(TRAFFIC_PROFILE):
@@ -90,7 +92,7 @@ def measured_traffic(B):
                 kv[k.strip()] = v.strip()
         if kv.get("kernel_sources_sha256") != kernel_sources_sha256():
             return None
-        if int(kv.get("batch", -1)) != B:
+        if int(kv.get("batch", -1)) != B or kv.get("config") != config:
             return None
         return int(float(kv["hbm_bytes_per_launch"]))
     except (OSError, KeyError, ValueError):
@@ -322,7 +324,7 @@ def main():
         "frac_of_roofline": round(roofline_us(B, D, V) / us, 4),
         "roofline": {"bound": "hbm", "achieved": round(achieved_gbs, 1), "peak": HBM_PEAK_GBS,
                      "unit": "GB/s", "frac": round(achieved_gbs / HBM_PEAK_GBS, 4),
-                     "traffic": measured_traffic(B),
+                     "traffic": measured_traffic(B, fsl.config_name(fsl.selected_config(B, D, V))),
                      "kernel": fsl.config_name(fsl.selected_config(B, D, V)),
                      "kernel_sources_sha256": kernel_sources_sha256()[:16],
                      "kernel_avg_us": round(k_us, 2), "kernel_min_us": round(k_lo * 1e3, 2),

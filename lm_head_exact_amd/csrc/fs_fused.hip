@@ -220,6 +220,7 @@ int fused_auto_config(int32_t B, int32_t D, int32_t V) {
   static const int lds128 = config_id("lds_mr4_nt8_nw4_kc64_p4_wb1_br4");
   static const int lds256 = config_id("lds_mr2_nt16_nw4_kc64_p4_wb1_br4");
   static const int lds_big = config_id("lds_mr2_nt16_nw4_kc64_p4_ntl0");
+  static const int lds_narrow = config_id("lds_mr2_nt8_nw4_kc64_p8_wb1_br4");
   static const int stream_small = config_id("stream_mr4_nt1_nw4_p4_ntl0");
   static const int stream_big = config_id("stream_mr2_nt4_nw4_p4_ntl0");
   for (int id : persist)
@@ -229,6 +230,14 @@ int fused_auto_config(int32_t B, int32_t D, int32_t V) {
   const Pick p = B <= 64 ? Pick{dma64, lds64} : (B <= 128 ? Pick{dma128, lds128} : Pick{dma256, lds256});
   constexpr double kMinFill = 0.85;
   if (fused_config_supports(p.dma, B, D) && one_per_cu_fill(p.dma, V) >= kMinFill) return p.dma;
+  // a short vocabulary (one shard of a split head) gives the 256-row batch tile
+  // too few blocks: two batch blocks of 128 rows keep twice as many CUs busy
+  // (W is then read twice, mostly from cache)
+  const int cus = device_cus();
+  if (B > 128 && cus > 0 && fused_config_supports(lds_narrow, B, D) &&
+      (static_cast<long>(V) + fused_rows_per_block(p.lds) - 1) / fused_rows_per_block(p.lds) <
+          static_cast<long>(cus))
+    return lds_narrow;
   if (fused_config_supports(p.lds, B, D)) return p.lds;
   if (B > 64 && fused_config_supports(lds_big, B, D)) return lds_big;
   return B <= 16 ? stream_small : stream_big;
