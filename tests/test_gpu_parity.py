@@ -207,3 +207,17 @@ def test_full_workloads_sampled_rows(wlk, B):
         assert np.all((ids >= lo) & (ids < hi))
     del h, W
     torch.cuda.empty_cache()
+
+
+@pytest.mark.parametrize("B,D,V,off", [
+    (4096, 256, 600, 0),                 # sixteen 256-row batch tiles
+    (3, 256, 2000, 2**31 - 1 - 2000),    # the vocabulary ends at id 2^31 - 2
+    (1, 8, 1, 2**31 - 2),                # one id, the largest the ABI admits
+])
+def test_maximum_sizes(B, D, V, off):
+    """Extremes of the argument ranges: a large batch over many batch blocks,
+    global ids at the top of the int32 range (the shifted grid and the
+    Philox counter near 2^29 blocks), the smallest problem."""
+    h, W, T = _rand_inputs(B, D, V, seed=B + V)
+    rows = None if B <= 64 else sample_rows(B, k=24, seed=1)
+    _run_and_check(h, W, T, seed=123, step=456, off=off, rows=rows, label=f"max B{B} V{V} off{off}")
