@@ -84,10 +84,17 @@ def _load():
         lib.oracle_merge_lse.restype = None
         lib.oracle_lse_logits.argtypes = [vp, i32, vp, i32, vp]
         lib.oracle_lse_logits.restype = None
+        lib.oracle_set_threads.argtypes = [ctypes.c_int]
+        lib.oracle_set_threads.restype = None
         lib.oracle_max_threads.argtypes = []
         lib.oracle_max_threads.restype = ctypes.c_int
         _lib = lib
     return _lib
+
+
+def set_threads(n: int) -> None:
+    """Threads the oracle's parallel loops use from now on (n <= 0: all)."""
+    _load().oracle_set_threads(int(n))
 
 
 def max_threads() -> int:

@@ -428,3 +428,8 @@ ORACLE_EXPORT void oracle_lse_logits(const float* z, int32_t V, const float* T, 
     out_lse[i] = (float)lse;
   }
 }
+
+/* Threads later OpenMP regions of the oracle use (n <= 0: the default).   */
+ORACLE_EXPORT void oracle_set_threads(int n) {
+  omp_set_num_threads(n > 0 ? n : omp_get_num_procs());
+}
