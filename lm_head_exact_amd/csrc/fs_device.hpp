@@ -193,11 +193,6 @@ __device__ __forceinline__ float row_inv_temperature(float T) {
   return row_is_greedy(T) ? 1.0f : __fdiv_rn(1.0f, T);
 }
 
-// Perturbed score of one logit: fp32 multiply then fp32 add, kept as two
-// separately rounded operations (no contraction into a fused multiply-add).
-__device__ __forceinline__ float perturbed_score(float z, float inv_t, float g) {
-  return __fadd_rn(__fmul_rn(z, inv_t), g);
-}
 
 // Pushes the scores of four consecutive logits z (local vocabulary rows
 // v0 .. v0+3, global ids gv0 .. gv0+3 with gv0 % 4 == 0, batch row `row`)
