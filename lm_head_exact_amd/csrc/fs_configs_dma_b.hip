@@ -13,6 +13,11 @@ int fused_configs_dma_b(const FusedConfig** out) {
       FS_DMAR(2, 16, 8, 64, 4, 4, 4, 2),
       FS_DMAR(4, 8, 8, 64, 4, 3, 4, 2),
       FS_DMAR(4, 4, 8, 64, 4, 3, 4, 2),
+      FS_DMAG(5, 4, 8, 64, 4, 3, 4, 2),
+      FS_DMAG(5, 8, 8, 64, 2, 3, 4, 2),
+      FS_DMAG(1, 4, 4, 64, 8, 3, 4, 2),
+      FS_DMAG(1, 16, 4, 64, 8, 3, 4, 2),
+      FS_DMAG(1, 8, 4, 64, 8, 3, 4, 2),
   };
   *out = k;
   return static_cast<int>(sizeof(k) / sizeof(k[0]));

@@ -212,10 +212,17 @@ int fused_auto_config(int32_t B, int32_t D, int32_t V) {
                                 config_id("persist_nt1_nw8_ks32_p8")};
   static const int ksplit = config_id("ksplit_mr1_nt1_nw4_p8_ntl0");
   // batch-tiled loops: the DMA-staged loop (one 8-wave block per CU) when its
-  // grid fills the CUs, else the LDS loop (smaller blocks, two per CU)
+  // grid fills the CUs; for a short vocabulary the same loop on 64-row blocks
+  // of four waves; else the LDS loop (smaller blocks, two per CU)
   static const int dma64 = config_id("dma_mr4_nt4_nw8_kc64_p4_s3_br4_g2");
+  static const int dma64_tall = config_id("dma_mr5_nt4_nw8_kc64_p4_s3_br4_g2");
   static const int dma128 = config_id("dma_mr4_nt8_nw8_kc64_p4_s3_br4_g2");
+  static const int dma128_tall = config_id("dma_mr5_nt8_nw8_kc64_p2_s3_br4_g2");
   static const int dma256 = config_id("dma_mr2_nt16_nw8_kc64_p4_s4_br4_g2");
+  static const int dma256_kc128 = config_id("dma_mr2_nt16_nw8_kc128_p4_s2_br4_g2");
+  static const int dma64_short = config_id("dma_mr1_nt4_nw4_kc64_p8_s3_br4_g2");
+  static const int dma128_short = config_id("dma_mr1_nt8_nw4_kc64_p8_s3_br4_g2");
+  static const int dma256_short = config_id("dma_mr1_nt16_nw4_kc64_p8_s3_br4_g2");
   static const int lds64 = config_id("lds_mr2_nt4_nw4_kc64_p4_ntl0");
   static const int lds128 = config_id("lds_mr4_nt8_nw4_kc64_p4_wb1_br4");
   static const int lds256 = config_id("lds_mr2_nt16_nw4_kc64_p4_wb1_br4");
@@ -226,18 +233,32 @@ int fused_auto_config(int32_t B, int32_t D, int32_t V) {
   for (int id : persist)
     if (fused_config_supports(id, B, D)) return id;
   if (B <= 8 && fused_config_supports(ksplit, B, D)) return ksplit;
-  struct Pick { int dma, lds; };
-  const Pick p = B <= 64 ? Pick{dma64, lds64} : (B <= 128 ? Pick{dma128, lds128} : Pick{dma256, lds256});
-  constexpr double kMinFill = 0.85;
-  if (fused_config_supports(p.dma, B, D) && one_per_cu_fill(p.dma, V) >= kMinFill) return p.dma;
-  // a short vocabulary (one shard of a split head) gives the 256-row batch tile
-  // too few blocks: two batch blocks of 128 rows keep twice as many CUs busy
-  // (W is then read twice, mostly from cache)
+  // DMA candidates per batch width, first choice first: 512-row blocks, else
+  // 640-row blocks where those fill the CUs better (a vocabulary of ~152k
+  // rows gives 297 blocks of 512, two rounds on 256 CUs, but 238 of 640).
+  // At 256 batch rows, rows longer than 4096 run faster with 128-wide staged
+  // chunks (2-3% in sweeps at D = 5120 and 8192; equal at 4096).
+  //
+  // Every candidate sums each logit's products in k order in one wave, like
+  // the LDS loops below: the choice may depend on V, so a vocabulary shard
+  // gets the same bits as the same rows inside a whole-vocabulary call.
+  struct Pick { int dma[2]; int dma_short; int lds; };
+  const Pick p = B <= 64    ? Pick{{dma64, dma64_tall}, dma64_short, lds64}
+                 : B <= 128 ? Pick{{dma128, dma128_tall}, dma128_short, lds128}
+                            : Pick{{D <= 4096 ? dma256 : dma256_kc128, dma256}, dma256_short, lds256};
+  // below three quarters of the CUs busy on average over the rounds the LDS
+  // loop's smaller blocks win (sweeps: 0.58 loses by 15-30%, 0.77 wins by 2-5%)
+  constexpr double kMinFill = 0.75;
+  for (int id : p.dma)
+    if (fused_config_supports(id, B, D) && one_per_cu_fill(id, V) >= kMinFill) return id;
+  // a short vocabulary (one shard of a split head) leaves CUs idle even under
+  // the LDS loop's blocks: 64-row blocks of four waves fill them and still
+  // read each W row once per batch block
   const int cus = device_cus();
-  if (B > 128 && cus > 0 && fused_config_supports(lds_narrow, B, D) &&
-      (static_cast<long>(V) + fused_rows_per_block(p.lds) - 1) / fused_rows_per_block(p.lds) <
-          static_cast<long>(cus))
-    return lds_narrow;
+  const bool short_v = cus > 0 && (static_cast<long>(V) + fused_rows_per_block(p.lds) - 1) /
+                                          fused_rows_per_block(p.lds) < static_cast<long>(cus);
+  if (short_v && fused_config_supports(p.dma_short, B, D)) return p.dma_short;
+  if (short_v && B > 128 && fused_config_supports(lds_narrow, B, D)) return lds_narrow;
   if (fused_config_supports(p.lds, B, D)) return p.lds;
   if (B > 64 && fused_config_supports(lds_big, B, D)) return lds_big;
   return B <= 16 ? stream_small : stream_big;

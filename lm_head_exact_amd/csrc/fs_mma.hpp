@@ -512,11 +512,21 @@ struct DmaLoop {
       static_for<MR>([&](auto m) FS_INLINE { ring[p][m] = load_frag(arow[m] + q * 32); });
     });
     __builtin_amdgcn_sched_barrier(0);
-    wait_vm<(S - 2) * IPW + P * MR>();  // chunk 0 staged
+    // Chunk 0 staged.  The count leaves only chunks 1 .. S-2 in flight and
+    // not the W ring: the ring loads read memory the compiler knows to be
+    // unchanging, so it may still move them below this wait and the barrier
+    // (it does when the loop below could run zero times); counted here they
+    // would then let chunk 0 be read before it lands.  With the ring issued
+    // first, the wait also covers the ring, whose first slot the first MFMA
+    // needs at once anyway.
+    wait_vm<(S - 2) * IPW>();
     barrier();
 
+    // nch >= U (supports), so the body runs at least once: no branch around
+    // the loop that would invite the compiler to sink the prologue into it
     int slot_c = 0;  // ring slot of chunk c
-    for (int c0 = 0; c0 < nch; c0 += U) {
+    int c0 = 0;
+    do {
       static_for<U>([&](auto u) FS_INLINE {
         const int c = c0 + u;
         const int slot_n = slot_c == 0 ? S - 1 : slot_c - 1;  // slot of chunk c + S - 1
@@ -548,7 +558,8 @@ struct DmaLoop {
         barrier();            // ... and every wave's; slot c is free again
         slot_c = slot_c == S - 1 ? 0 : slot_c + 1;
       });
-    }
+      c0 += U;
+    } while (c0 < nch);
     wait_vm<0>();  // the trailing (clamped) staging loads land before LDS is reused
   }
 };

@@ -61,7 +61,7 @@ def _num_configs():
     try:
         return fsl.num_configs()
     except Exception:  # library not built: collection must still succeed
-        return 29
+        return 34
 
 
 @pytest.mark.parametrize("cfg", range(_num_configs()))
