@@ -220,6 +220,7 @@ int fused_auto_config(int32_t B, int32_t D, int32_t V) {
   static const int dma128_tall = config_id("dma_mr5_nt8_nw8_kc64_p2_s3_br4_g2");
   static const int dma256 = config_id("dma_mr2_nt16_nw8_kc64_p4_s4_br4_g2");
   static const int dma256_kc128 = config_id("dma_mr2_nt16_nw8_kc128_p4_s2_br4_g2");
+  static const int dma_paired = config_id("dmapair_mr2_nt16_nw8_kc128_p4_s2_br4_g2");
   static const int dma64_short = config_id("dma_mr1_nt4_nw4_kc64_p8_s3_br4_g2");
   static const int dma128_short = config_id("dma_mr1_nt8_nw4_kc64_p8_s3_br4_g2");
   static const int dma256_short = config_id("dma_mr1_nt16_nw4_kc64_p8_s3_br4_g2");
@@ -237,15 +238,20 @@ int fused_auto_config(int32_t B, int32_t D, int32_t V) {
   // 640-row blocks where those fill the CUs better (a vocabulary of ~152k
   // rows gives 297 blocks of 512, two rounds on 256 CUs, but 238 of 640).
   // At 256 batch rows, rows longer than 4096 run faster with 128-wide staged
-  // chunks (2-3% in sweeps at D = 5120 and 8192; equal at 4096).
+  // chunks (2-3% in sweeps at D = 5120 and 8192; equal at 4096).  Above 256
+  // batch rows the batch blocks of one vocabulary tile run side by side on
+  // one XCD and share its W rows through L2 (9-12% at B = 384 and 512 at
+  // D = 4096, 5120 and 8192).
   //
   // Every candidate sums each logit's products in k order in one wave, like
   // the LDS loops below: the choice may depend on V, so a vocabulary shard
   // gets the same bits as the same rows inside a whole-vocabulary call.
   struct Pick { int dma[2]; int dma_short; int lds; };
+  const int dma256_first = D <= 4096 ? dma256 : dma256_kc128;
   const Pick p = B <= 64    ? Pick{{dma64, dma64_tall}, dma64_short, lds64}
                  : B <= 128 ? Pick{{dma128, dma128_tall}, dma128_short, lds128}
-                            : Pick{{D <= 4096 ? dma256 : dma256_kc128, dma256}, dma256_short, lds256};
+                 : B <= 256 ? Pick{{dma256_first, dma256}, dma256_short, lds256}
+                            : Pick{{dma_paired, dma256_first}, dma256_short, lds256};
   // below three quarters of the CUs busy on average over the rounds the LDS
   // loop's smaller blocks win (sweeps: 0.58 loses by 15-30%, 0.77 wins by 2-5%)
   constexpr double kMinFill = 0.75;

@@ -11,7 +11,8 @@
 // (hierarchical) sampler.
 //
 // Grid: x = vocabulary blocks of Loop::kRowsPerBlock rows, y = batch blocks of
-// NT * 16 rows.  The main loop (fs_mma.hpp) is a policy that leaves each
+// NT * 16 rows (an XcdPaired loop uses a 1-D grid of the same blocks; see
+// block_tile below).  The main loop (fs_mma.hpp) is a policy that leaves each
 // wave with MFMA accumulators for MR * 16 vocabulary rows x NT * 16 batch
 // rows; the epilogue runs in registers on those accumulators and the block
 // writes one (max, argmax) partial per batch row to part_[val|idx][b][block].
@@ -20,10 +21,51 @@
 // (fs_configs_*.hip) so that they compile in parallel.
 #pragma once
 
+#include <type_traits>
+
 #include "fs_internal.hpp"
 #include "fs_mma.hpp"
 
 namespace fs {
+
+// A main loop wrapped in XcdPaired runs on a 1-D grid in which the batch
+// blocks of one vocabulary tile are 8 block ids apart.  Blocks are dealt to
+// the 8 XCDs round robin, so those blocks run on one XCD at nearly the same
+// time, and all but the first find the tile's W rows in that XCD's L2: a
+// narrower batch tile (more MFMAs per B fragment read from LDS) without
+// reading W from HBM once per batch block.
+template <class L>
+struct XcdPaired : L {
+  static constexpr bool kXcdPaired = true;
+};
+template <class L, class = void>
+struct is_xcd_paired : std::false_type {};
+template <class L>
+struct is_xcd_paired<L, std::void_t<decltype(L::kXcdPaired)>>
+    : std::bool_constant<L::kXcdPaired> {};
+
+constexpr int kXcds = 8;
+
+// Batch blocks per call, and grid blocks per launch.
+template <class Loop>
+__host__ __device__ inline int batch_blocks(int32_t B) {
+  return (B + Loop::kBlockCols - 1) / Loop::kBlockCols;
+}
+
+// (vocabulary tile, batch block) of this block; tile >= S marks a padding
+// block of the paired grid.
+template <class Loop>
+__device__ __forceinline__ void block_tile(const SampleArgs& a, int& tile, int& bblock) {
+  if constexpr (is_xcd_paired<Loop>::value) {
+    const int per_group = kXcds * batch_blocks<Loop>(a.B);
+    const int g = blockIdx.x / per_group, w = blockIdx.x % per_group;
+    tile = g * kXcds + w % kXcds;
+    bblock = w / kXcds;
+  } else {
+    tile = blockIdx.x;
+    bblock = blockIdx.y;
+  }
+}
 
 template <class Loop, bool LSE>
 __global__ __launch_bounds__(Loop::NW * kWave)
@@ -36,8 +78,11 @@ __attribute__((amdgpu_waves_per_eu(Loop::kWavesPerSimd))) void fused_sample_kern
   // The vocabulary grid starts vocab_offset mod 4 rows before row 0, so that
   // every lane's four consecutive rows begin at a global id divisible by 4.
   const int shift = a.vocab_offset & 3;
-  const int row0 = Loop::row0(blockIdx.x, wave) - shift;
-  const int block_col0 = blockIdx.y * Loop::kBlockCols;
+  int tile, bblock;
+  block_tile<Loop>(a, tile, bblock);
+  if (tile >= a.S) return;  // padding block of a paired grid (block-uniform)
+  const int row0 = Loop::row0(tile, wave) - shift;
+  const int block_col0 = bblock * Loop::kBlockCols;
 
   const int col0 = block_col0 + Loop::col_off(wave);  // this wave's first batch row
   // The temperatures of the wave's batch rows are loaded all at once, before
@@ -112,7 +157,7 @@ __attribute__((amdgpu_waves_per_eu(Loop::kWavesPerSimd))) void fused_sample_kern
 #pragma unroll
     for (int w = 0; w < NW; ++w)
       if (Loop::col_off(w) == c - c % (NT * 16)) m.push(s_val[w][c % (NT * 16)], s_idx[w][c % (NT * 16)]);
-    const size_t o = static_cast<size_t>(b) * a.S + blockIdx.x;
+    const size_t o = static_cast<size_t>(b) * a.S + tile;
     a.part_val[o] = m.v;
     a.part_idx[o] = m.i;
   }
@@ -134,7 +179,7 @@ __attribute__((amdgpu_waves_per_eu(Loop::kWavesPerSimd))) void fused_sample_kern
       for (int w = 0; w < NW; ++w)
         if (Loop::col_off(w) == c - c % (NT * 16))
           l.merge(s_val[w][c % (NT * 16)], __int_as_float(s_idx[w][c % (NT * 16)]));
-      a.part_lse[static_cast<size_t>(b) * a.S + blockIdx.x] = l.value(row_is_greedy(a.temperature[b]));
+      a.part_lse[static_cast<size_t>(b) * a.S + tile] = l.value(row_is_greedy(a.temperature[b]));
     }
   }
 }
@@ -305,7 +350,9 @@ hipError_t launch_cfg(SampleArgs& a, hipStream_t stream) {
     if (attr != hipSuccess) return attr;
   }
   a.S = (a.V + (a.vocab_offset & 3) + rows - 1) / rows;
-  const dim3 grid(a.S, (a.B + Loop::kBlockCols - 1) / Loop::kBlockCols);
+  const int nb = batch_blocks<Loop>(a.B);
+  const dim3 grid = is_xcd_paired<Loop>::value ? dim3((a.S + kXcds - 1) / kXcds * kXcds * nb)
+                                               : dim3(a.S, nb);
   const dim3 block(Loop::NW * kWave);
   if (a.part_lse == nullptr)
     fused_sample_kernel<Loop, false><<<grid, block, smem, stream>>>(a);
@@ -387,6 +434,9 @@ constexpr FusedConfig make_persist(const char* name, int order) {
 #define FS_DMAR(MR, NT, NW, KC, P, S, BR, G)                                                  \
   make_cfg<DmaLoop<MR, NT, NW, KC, P, S, BR, G, true>>(                                      \
       "dmarot_mr" #MR "_nt" #NT "_nw" #NW "_kc" #KC "_p" #P "_s" #S "_br" #BR "_g" #G, 0)
+#define FS_DMAP(MR, NT, NW, KC, P, S, BR, G)                                                  \
+  make_cfg<XcdPaired<DmaLoop<MR, NT, NW, KC, P, S, BR, G>>>(                                 \
+      "dmapair_mr" #MR "_nt" #NT "_nw" #NW "_kc" #KC "_p" #P "_s" #S "_br" #BR "_g" #G, 0)
 #define FS_PERSIST(NT, NW, KS, P) \
   make_persist<Persist<NT, NW, KS, P>>("persist_nt" #NT "_nw" #NW "_ks" #KS "_p" #P, 100 + NW)
 
