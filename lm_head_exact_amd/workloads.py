@@ -162,3 +162,30 @@ def bf16_bits(t: torch.Tensor):
     """Raw bf16 bit patterns of a tensor as a host numpy uint16 array."""
     assert t.dtype == torch.bfloat16
     return t.detach().cpu().contiguous().view(torch.int16).numpy().view("uint16")
+
+
+def make_confident_w(wl: Workload, h: torch.Tensor, chunk_rows: int, later_std: float,
+                     gain: float = 1.0, seed: Optional[int] = None,
+                     device="cpu") -> torch.Tensor:
+    """W (V x D) for the online sampler's early-finalisation case.
+
+    A stand-in for a confident model whose rare tokens have small output
+    embeddings: row b < B of the first chunk (rows [0, chunk_rows)) is
+    parallel to batch row b of ``h``, scaled to ``gain`` times the norm a
+    typical row of N(0, w_std^2) has (w_std * sqrt(D)); the other rows of the first chunk
+    are N(0, w_std^2); every later row is N(0, later_std^2).
+    """
+    B, D = h.shape
+    assert D == wl.D and B <= chunk_rows <= wl.V
+    W = make_w(wl, device, seed=seed)
+    g = _gen((wl.w_seed if seed is None else seed) + 7, device)
+    later = wl.V - chunk_rows
+    step = max(1, (1 << 26) // D)
+    for r0 in range(0, later, step):
+        r1 = min(later, r0 + step)
+        blk = torch.randn(r1 - r0, D, generator=g, device=device, dtype=torch.float32)
+        W[chunk_rows + r0:chunk_rows + r1] = (blk * later_std).to(torch.bfloat16)
+    x = h.to(device=device, dtype=torch.float32)
+    x = x / x.norm(dim=1, keepdim=True).clamp_min(1e-30) * (gain * wl.w_std * D ** 0.5)
+    W[:B] = x.to(torch.bfloat16)
+    return W

@@ -84,6 +84,13 @@ def _load():
         lib.oracle_merge_lse.restype = None
         lib.oracle_lse_logits.argtypes = [vp, i32, vp, i32, vp]
         lib.oracle_lse_logits.restype = None
+        lib.oracle_gumbel_max.argtypes = []
+        lib.oracle_gumbel_max.restype = ctypes.c_double
+        lib.oracle_max_row_norm.argtypes = [vp, i32, i32]
+        lib.oracle_max_row_norm.restype = ctypes.c_double
+        lib.oracle_sample_online.argtypes = [vp, vp, i32, i32, vp, i32, vp, u64, u64, vp, i32,
+                                             vp, vp, vp]
+        lib.oracle_sample_online.restype = None
         lib.oracle_set_threads.argtypes = [ctypes.c_int]
         lib.oracle_set_threads.restype = None
         lib.oracle_max_threads.argtypes = []
@@ -298,3 +305,42 @@ def merge_lse(val, ids, lse, T, seed, step):
                              int(step), _ptr(out_id), _ptr(out_val), _ptr(out_lse),
                              _ptr(out_gap))
     return out_id, out_val, out_lse, out_gap
+
+
+# ---------------------------------------------------------------------------
+# Online (chunked) sampler with early finalisation: oracle.c, "Online
+# (chunked) sampler with early finalisation".
+# ---------------------------------------------------------------------------
+def gumbel_max():
+    """Largest value of the Gumbel map on the uniform grid, -log(-log(1 - 2^-24))."""
+    return float(_load().oracle_gumbel_max())
+
+
+def max_row_norm(W):
+    """Largest Euclidean row norm of W (bf16 bits, V x D), fp64."""
+    W = _c(W, np.uint16)
+    V, D = W.shape
+    return float(_load().oracle_max_row_norm(_ptr(W), V, D))
+
+
+def sample_online(h, W, T, seed, step, cuts, vocab_offset=0, rows=None):
+    """Chunks W[cuts[c]:cuts[c+1]] in order with early finalisation per row.
+    Returns (ids, val, chunks_used)."""
+    h = _c(h, np.uint16)
+    W = _c(W, np.uint16)
+    T = _c(T, np.float32)
+    cuts = _c(cuts, np.int32)
+    B, D = h.shape
+    V, D2 = W.shape
+    assert D == D2 and T.shape == (B,)
+    assert cuts[0] == 0 and cuts[-1] == V and np.all(np.diff(cuts) > 0)
+    r = None if rows is None else _c(rows, np.int32)
+    n = B if r is None else r.size
+    ids = np.empty(n, np.int32)
+    val = np.empty(n, np.float32)
+    used = np.empty(n, np.int32)
+    if n:
+        _load().oracle_sample_online(_ptr(h), _ptr(W), D, int(vocab_offset), _ptr(cuts),
+                                     cuts.size - 1, _ptr(T), int(seed), int(step), _ptr(r), n,
+                                     _ptr(ids), _ptr(val), _ptr(used))
+    return ids, val, used

@@ -429,6 +429,96 @@ ORACLE_EXPORT void oracle_lse_logits(const float* z, int32_t V, const float* T, 
   }
 }
 
+/* ---------------------------------------------------------------------- */
+/* Online (chunked) sampler with early finalisation                         */
+/* ---------------------------------------------------------------------- */
+/* The vocabulary arrives as consecutive chunks; the running (max, argmax)
+ * is the Gumbel-max over the chunks seen so far, and the sample may be
+ * finalised as soon as no later chunk can overtake it (wiki summary,
+ * "Method": the streaming sampler of the online setting).  The pages give
+ * no bound; the reading built here:
+ *   - a later logit obeys z = h . W_v <= |h| * R, R the largest row norm of
+ *     the later chunks (Cauchy-Schwarz);
+ *   - a noise value is at most g_max, the largest value of the Gumbel map on
+ *     the uniform grid, -log(-log(1 - 2^-24));
+ *   - row b is final after chunk c when its running best exceeds
+ *     (|h_b| * R_c * (1/T) + g_max) * (1 + 2^-8) (greedy rows: |h_b| * R_c *
+ *     (1 + 2^-8), no scaling and no noise).  The factor 1 + 2^-8 is a safety
+ *     margin for rounding: fp32 logits, scores and norms stay below the bound.
+ * The samples are those of oracle_sample over the whole vocabulary, whatever
+ * the chunks; this function also reports, per row, how many chunks were
+ * needed.                                                                  */
+ORACLE_EXPORT double oracle_gumbel_max(void) { return -log(-log(1.0 - ldexp(1.0, -24))); }
+
+/* Euclidean norm of a bf16 row, fp64.                                      */
+static double row_norm(const uint16_t* x, int32_t D) {
+  double s = 0.0;
+  for (int32_t d = 0; d < D; ++d) {
+    double v = bf16_to_double(x[d]);
+    s += v * v;
+  }
+  return sqrt(s);
+}
+
+/* Largest row norm of W (V x D), fp64.                                     */
+ORACLE_EXPORT double oracle_max_row_norm(const uint16_t* W, int32_t V, int32_t D) {
+  double m = 0.0;
+  for (int32_t v = 0; v < V; ++v) {
+    double n = row_norm(W + (size_t)v * D, D);
+    if (n > m) m = n;
+  }
+  return m;
+}
+
+/* cuts[0] = 0 < cuts[1] < ... < cuts[n_chunks] = V delimit the chunks of W
+ * (V x D).  Per listed row: sampled id, winning score, chunks processed.   */
+ORACLE_EXPORT void oracle_sample_online(const uint16_t* h, const uint16_t* W, int32_t D,
+                                        int32_t vocab_offset, const int32_t* cuts,
+                                        int32_t n_chunks, const float* T, uint64_t seed,
+                                        uint64_t step, const int32_t* rows, int32_t n_rows,
+                                        int32_t* out_id, float* out_val,
+                                        int32_t* out_chunks) {
+  const double margin = 1.0 + ldexp(1.0, -8);
+  const double g_max = oracle_gumbel_max();
+  /* later[c]: the largest row norm in chunks c+1 .. n_chunks-1 (0 if none) */
+  double* later = (double*)malloc(sizeof(double) * (size_t)n_chunks);
+  double m = 0.0;
+  for (int32_t c = n_chunks - 1; c >= 0; --c) {
+    later[c] = m;
+    double mc = oracle_max_row_norm(W + (size_t)cuts[c] * D, cuts[c + 1] - cuts[c], D);
+    if (mc > m) m = mc;
+  }
+#pragma omp parallel for schedule(dynamic, 1)
+  for (int32_t i = 0; i < n_rows; ++i) {
+    int32_t b = rows ? rows[i] : i;
+    float Tb = T[b];
+    int greedy = is_greedy(Tb);
+    float inv_T = greedy ? 1.0f : 1.0f / Tb;
+    double hn = row_norm(h + (size_t)b * D, D);
+    running_max r;
+    rm_init(&r);
+    int32_t used = n_chunks;
+    for (int32_t c = 0; c < n_chunks; ++c) {
+      for (int32_t v = cuts[c]; v < cuts[c + 1]; ++v) {
+        float z = oracle_logit(h + (size_t)b * D, W + (size_t)v * D, D);
+        int32_t gv = vocab_offset + v;
+        rm_push(&r, score(z, Tb, inv_T, seed, step, (uint32_t)b, (uint32_t)gv), gv);
+      }
+      if (c == n_chunks - 1) break;
+      double bound = greedy ? hn * later[c] * margin
+                            : (hn * later[c] * (double)inv_T + g_max) * margin;
+      if ((double)r.best > bound) {
+        used = c + 1;
+        break;
+      }
+    }
+    out_id[i] = r.best_id;
+    out_val[i] = r.best;
+    out_chunks[i] = used;
+  }
+  free(later);
+}
+
 /* Threads later OpenMP regions of the oracle use (n <= 0: the default).   */
 ORACLE_EXPORT void oracle_set_threads(int n) {
   omp_set_num_threads(n > 0 ? n : omp_get_num_procs());
