@@ -8,12 +8,14 @@ already resident in device memory and a fresh (seed, step) per step.  The
 headline line is B = 32; the same line carries the B = 1 .. 256 sweep, the
 unfused baseline (logits and probabilities through device memory) timed the
 same way, the grouped (hierarchical) sampler over 1 and 8 vocabulary groups,
-the Qwen3-shaped, large-batch and vocabulary-shard heads, the fused kernel's
+the online sampler with early finalisation (8 vocabulary chunks), the
+Qwen3-shaped, large-batch and vocabulary-shard heads, the fused kernel's
 roofline fraction and the CPU oracle's rate.
 
 Prints ONE JSON line on stdout.  Usage:
   python bench.py [--gpus 1] [--steps K] [--warmup W] [--batch 32]
-                  [--sweep 1,2,4,...] [--no-cpu-baseline] [--profile-pass]
+                  [--sweep 1,2,4,...] [--no-cpu-baseline] [--no-unfused]
+                  [--no-grouped] [--no-online] [--no-workloads] [--profile-pass]
 --profile-pass runs a short fixed sequence for rocprofv3 (a few fused steps
 plus a 1 GiB device copy used to calibrate the HBM byte counters) and exits.
 """
@@ -44,6 +46,7 @@ def parse():
     ap.add_argument("--no-unfused", action="store_true")
     ap.add_argument("--no-grouped", action="store_true")
     ap.add_argument("--no-workloads", action="store_true")
+    ap.add_argument("--no-online", action="store_true")
     ap.add_argument("--profile-pass", action="store_true")
     return ap.parse_args()
 
@@ -251,6 +254,61 @@ def main():
                         "fs_sample_us_per_step": plain})
         del h_g, T_g, pv, pi, pl, ws, outs
 
+    # Online sampler with early finalisation: fs_sample_online per step over
+    # the vocabulary in 8 chunks of 16032 rows, or in 2 chunks (the first
+    # 16032 rows, then the rest), replayed as a captured graph (1 + 2 chunks
+    # launches).  "confident" weights (the first chunk holds a row aligned
+    # with each hidden state, later rows are small) finalise every row after
+    # the first chunk; the random weights never finalise early, which
+    # measures the cost of chunking.  The bounds are computed once per weight
+    # matrix and chunking (timed separately).
+    online = []
+    if not args.no_online:
+        splits = (list(range(0, V + 1, V // 8)), [0, V // 8, V])
+        for b in (B, 256):
+            h_o = wl.make_h(wlk, b, dev)
+            T_o = wl.make_temperature(wlk, b, dev)
+            outs = (torch.empty(b, dtype=torch.int32, device=dev),
+                    torch.empty(b, dtype=torch.float32, device=dev),
+                    torch.empty(b, dtype=torch.int32, device=dev))
+            for kind in ("confident", "random"):
+                W_o = (wl.make_confident_w(wlk, h_o, chunk_rows=V // 8, later_std=0.002,
+                                           device=dev) if kind == "confident" else W)
+                for cuts in splits:
+                    n_chunks = len(cuts) - 1
+                    bt = time_steps(torch, lambda i: fsl.online_bounds(W_o, cuts), 3, 1,
+                                    stream) * 1e3
+                    later = fsl.online_bounds(W_o, cuts)
+                    ws = fsl.alloc_workspace(fsl.online_workspace_bytes(b, D, V, n_chunks), dev)
+
+                    def ofn(i, h_o=h_o, T_o=T_o, W_o=W_o, cuts=cuts, later=later, outs=outs,
+                            ws=ws):
+                        seed, step = wlk.sampler_seed(i)
+                        fsl.sample_online(h_o, W_o, T_o, seed, step, cuts, later, out=outs,
+                                          workspace=ws)
+                    for i in range(3):
+                        ofn(i)
+                    torch.cuda.synchronize()
+                    graph = torch.cuda.CUDAGraph()
+                    with torch.cuda.graph(graph):
+                        ofn(11)
+                    ot = time_steps(torch, lambda i: graph.replay(),
+                                    max(10, args.sweep_steps // 2), 5,
+                                    torch.cuda.current_stream(dev)) * 1e3
+                    torch.cuda.synchronize()
+                    used = outs[2].float().mean().item()
+                    del graph
+                    plain = next((e["us_per_step"] for e in sweep if e["B"] == b), None)
+                    online.append({"B": b, "weights": kind, "chunks": n_chunks,
+                                   "first_chunk_rows": cuts[1],
+                                   "us_per_step": round(ot, 2),
+                                   "mean_chunks_used": round(used, 3),
+                                   "fs_sample_us_per_step": plain, "bounds_us": round(bt, 1)})
+                    del later, ws
+                del W_o
+            del h_o, T_o, outs
+            torch.cuda.empty_cache()
+
     # The other LM-head shapes (fused step only): Qwen3-shaped (D=5120,
     # V=151936, mixed temperatures with greedy rows), large batch (D=8192) and
     # one GPU's share of an 8-way vocabulary shard (D=8192, V=16032 at
@@ -344,6 +402,7 @@ def main():
         "cpu_baseline": cpu,
         "sweep": sweep,
         "grouped_lse": grouped,
+        "online": online,
         "other_workloads": workloads,
         "device": {"name": props.name, "cus": props.multi_processor_count,
                    "gcn_arch": getattr(props, "gcnArchName", "")},

@@ -148,6 +148,55 @@ FS_API fs_status fs_merge_lse(const float* partial_val, const int32_t* partial_i
                        const float* temperature, uint64_t seed, uint64_t step,
                        int32_t* out_ids, float* out_maxval, float* out_lse, void* stream);
 
+/* Online (chunked) sampler with early finalisation (wiki summary, "Method",
+ * last paragraph: in the online setting the sampler streams over pieces of
+ * the vocabulary and may finalise before it has seen them all).  The
+ * vocabulary is processed in the chunks W[cuts[c] .. cuts[c+1]), c = 0 ..
+ * n_chunks - 1, in order; the running (max, argmax) over the chunks seen so
+ * far is the Gumbel-max over them.  The pages state no stopping rule; the one
+ * used here follows from Cauchy-Schwarz: row b is final after chunk c once
+ * its running best exceeds
+ *     (|h_b| * later_norm[c] * fp32(1/T_b) + g_max) * (1 + 2^-8)
+ * (greedy rows: |h_b| * later_norm[c] * (1 + 2^-8)), where later_norm[c] is
+ * the largest row norm of W over the chunks after c and g_max =
+ * -log(-log(1 - 2^-24)) the largest Gumbel value of the noise field.  No later
+ * score can overtake such a row, so the ids and scores are those of
+ * fs_sample over the whole of W; only the work changes.  Once every row is
+ * final the remaining chunks' kernels return without reading their W rows.
+ *
+ * fs_online_bounds computes later_norm once per weight matrix and chunking:
+ *   W            bf16 [V][D], device, 16-byte aligned, D % 8 == 0
+ *   cuts         HOST int32 [n_chunks + 1]: 0 = cuts[0] < cuts[1] < ... <
+ *                cuts[n_chunks] = V; 1 <= n_chunks <= 65536
+ *   later_norm   fp64 [n_chunks], device, 8-byte aligned: later_norm[c] =
+ *                max over rows v >= cuts[c+1] of |W_v| (fp64 sums), and
+ *                later_norm[n_chunks - 1] = 0
+ *   workspace    >= fs_online_bounds_workspace_bytes(V, n_chunks) bytes
+ *
+ * fs_sample_online takes fs_sample's arguments plus
+ *   cuts, n_chunks  as above (HOST array), relative to W row 0: chunk c holds
+ *                global ids vocab_offset + cuts[c] .. vocab_offset + cuts[c+1] - 1
+ *   later_norm   from fs_online_bounds for the same W and cuts (device)
+ *   out_chunks   int32 [B], device: chunks folded into row b's result (the
+ *                chunk after which it became final, else n_chunks)
+ *   workspace    >= fs_online_workspace_bytes(B, D, V, n_chunks) bytes
+ * out_ids / out_maxval as fs_sample.  D <= 32768 (FS_ERR_UNSUPPORTED beyond:
+ * the margin 1 + 2^-8 covers the device's fp32 rounding of logits up to that
+ * length).  Other errors as fs_sample; a cuts array that does not partition
+ * [0, V) is FS_ERR_INVALID_ARG.  Both workspace-size functions return 0 for
+ * invalid arguments. */
+FS_API size_t fs_online_bounds_workspace_bytes(int32_t V, int32_t n_chunks);
+FS_API size_t fs_online_workspace_bytes(int32_t B, int32_t D, int32_t V, int32_t n_chunks);
+FS_API fs_status fs_online_bounds(const void* W, int32_t V, int32_t D, const int32_t* cuts,
+                                  int32_t n_chunks, double* later_norm, void* workspace,
+                                  size_t workspace_bytes, void* stream);
+FS_API fs_status fs_sample_online(const void* h, const void* W, int32_t B, int32_t D,
+                                  int32_t V, int32_t vocab_offset, const float* temperature,
+                                  uint64_t seed, uint64_t step, const int32_t* cuts,
+                                  int32_t n_chunks, const double* later_norm, int32_t* out_ids,
+                                  float* out_maxval, int32_t* out_chunks, void* workspace,
+                                  size_t workspace_bytes, void* stream);
+
 /* The standard unfused decode step the method replaces (wiki summary,
  * "Method", first paragraph): (1) matmul writing fp32 logits [B][V] to
  * device memory, (2) softmax of z / T writing probabilities, (3)+(4)

@@ -9,7 +9,8 @@ use and a missing build raises instead of falling back to anything else.
 _BINDING_NAMES = ("sample", "sample_partial", "merge", "sample_partial_lse", "merge_lse", "sample_unfused", "workspace_bytes",
                   "unfused_workspace_bytes", "library_path", "debug_noise", "debug_gumbel",
                   "num_configs", "config_name", "profile_enable", "profile_read", "force_config", "selected_config",
-                  "FlashSampleError", "alloc_workspace")
+                  "FlashSampleError", "alloc_workspace", "online_bounds", "sample_online",
+                  "online_workspace_bytes")
 __all__ = list(_BINDING_NAMES)
 
 

@@ -61,6 +61,11 @@ def lib():
         ("fs_sample_partial_lse", [vp, vp, i32, i32, i32, i32, vp, u64, u64, vp, vp, vp, vp,
                                    sz, vp], ctypes.c_int),
         ("fs_merge_lse", [vp, vp, vp, i32, i32, vp, u64, u64, vp, vp, vp, vp], ctypes.c_int),
+        ("fs_online_bounds_workspace_bytes", [i32, i32], sz),
+        ("fs_online_workspace_bytes", [i32, i32, i32, i32], sz),
+        ("fs_online_bounds", [vp, i32, i32, vp, i32, vp, vp, sz, vp], ctypes.c_int),
+        ("fs_sample_online", [vp, vp, i32, i32, i32, i32, vp, u64, u64, vp, i32, vp, vp, vp,
+                              vp, vp, sz, vp], ctypes.c_int),
         ("fs_debug_noise", [u64, u64, u32, u32, i64, vp, vp, vp], ctypes.c_int),
         ("fs_debug_gumbel", [vp, i64, vp, vp], ctypes.c_int),
         ("fs_num_configs", [], i32),
@@ -254,6 +259,68 @@ def merge(partial_val: torch.Tensor, partial_idx: torch.Tensor, out=None):
     _check(lib().fs_merge(_ptr(partial_val), _ptr(partial_idx), P, B, _ptr(ids), _ptr(val),
                           _stream(dev)))
     return ids, val
+
+
+def _host_cuts(cuts):
+    """cuts as a host int32 ctypes array (kept alive by the caller) and the chunk count."""
+    c = [int(x) for x in (cuts.tolist() if hasattr(cuts, "tolist") else cuts)]
+    if len(c) < 2:
+        raise ValueError("cuts needs at least two entries (0 and V)")
+    return (ctypes.c_int32 * len(c))(*c), len(c) - 1
+
+
+def online_bounds(W: torch.Tensor, cuts, workspace: Optional[torch.Tensor] = None):
+    """later_norm (fp64 [n_chunks], device) for the online sampler over the
+    chunks W[cuts[c]:cuts[c+1]]: the largest row norm after each chunk."""
+    _req(W, "W", torch.bfloat16, 2)
+    V, D = W.shape
+    arr, n = _host_cuts(cuts)
+    later = torch.empty(n, dtype=torch.float64, device=W.device)
+    if workspace is None:
+        workspace = alloc_workspace(int(lib().fs_online_bounds_workspace_bytes(V, n)), W.device)
+    _check(lib().fs_online_bounds(_ptr(W), V, D, arr, n, _ptr(later), _ptr(workspace),
+                                  workspace.numel() * workspace.element_size(),
+                                  _stream(W.device)))
+    return later
+
+
+def online_workspace_bytes(B: int, D: int, V: int, n_chunks: int) -> int:
+    return int(lib().fs_online_workspace_bytes(B, D, V, n_chunks))
+
+
+def sample_online(h, W, temperature, seed, step, cuts, later_norm, vocab_offset=0, out=None,
+                  workspace=None):
+    """Online sampler with early finalisation over the chunks W[cuts[c]:cuts[c+1]]:
+    returns (ids int32[B], maxval fp32[B], chunks int32[B])."""
+    _req(h, "h", torch.bfloat16, 2)
+    _req(W, "W", torch.bfloat16, 2)
+    _req(temperature, "temperature", torch.float32, 1)
+    _req(later_norm, "later_norm", torch.float64, 1)
+    B, D = h.shape
+    V, D2 = W.shape
+    if D2 != D:
+        raise ValueError(f"h is B x {D} but W is V x {D2}")
+    if temperature.shape[0] != B:
+        raise ValueError("temperature must have B entries")
+    arr, n = _host_cuts(cuts)
+    if later_norm.shape[0] != n:
+        raise ValueError("later_norm must have one entry per chunk")
+    dev = h.device
+    if out is None:
+        out = (torch.empty(B, dtype=torch.int32, device=dev),
+               torch.empty(B, dtype=torch.float32, device=dev),
+               torch.empty(B, dtype=torch.int32, device=dev))
+    ids, val, chunks = out
+    if len({t.device for t in (h, W, temperature, later_norm, ids, val, chunks)}) != 1:
+        raise ValueError("all tensors must be on one device")
+    if workspace is None:
+        workspace = alloc_workspace(online_workspace_bytes(B, D, V, n), dev)
+    _check(lib().fs_sample_online(
+        _ptr(h), _ptr(W), B, D, V, int(vocab_offset), _ptr(temperature),
+        int(seed) & (2**64 - 1), int(step) & (2**64 - 1), arr, n, _ptr(later_norm), _ptr(ids),
+        _ptr(val), _ptr(chunks), _ptr(workspace), workspace.numel() * workspace.element_size(),
+        _stream(dev)))
+    return ids, val, chunks
 
 
 def debug_noise(seed: int, step: int, row: int, gv0: int, n: int, device="cuda"):

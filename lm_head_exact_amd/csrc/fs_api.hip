@@ -4,6 +4,7 @@
 // assume the checked invariants (D % 8 == 0 and 16-byte aligned operands for
 // the 16-byte fragment loads, ids that fit in int32, enough workspace).
 #include <atomic>
+#include <cmath>
 #include <cstdarg>
 #include <cstdio>
 #include <cstdlib>
@@ -165,6 +166,38 @@ fs_status run_fused(const void* h, const void* W, int32_t B, int32_t D, int32_t 
   return FS_OK;
 }
 
+// ---- online sampler ----
+constexpr int32_t kMaxChunks = 1 << 16;
+// Longest rows for which the bound's margin 1 + 2^-8 covers the device's fp32
+// logit rounding (about D * 2^-24 relative).
+constexpr int32_t kMaxOnlineD = 32768;
+
+fs_status check_cuts(const int32_t* cuts, int32_t n_chunks, int32_t V, const char* who) {
+  if (!cuts) return fail(FS_ERR_INVALID_ARG, "%s: null cuts", who);
+  if (n_chunks < 1 || n_chunks > kMaxChunks)
+    return fail(FS_ERR_INVALID_ARG, "%s: n_chunks must be in [1, %d] (got %d)", who, kMaxChunks,
+                n_chunks);
+  if (cuts[0] != 0 || cuts[n_chunks] != V)
+    return fail(FS_ERR_INVALID_ARG, "%s: cuts must start at 0 and end at V=%d (got %d .. %d)",
+                who, V, cuts[0], cuts[n_chunks]);
+  for (int32_t c = 0; c < n_chunks; ++c)
+    if (cuts[c + 1] <= cuts[c])
+      return fail(FS_ERR_INVALID_ARG, "%s: cuts must increase strictly (cuts[%d]=%d, cuts[%d]=%d)",
+                  who, c, cuts[c], c + 1, cuts[c + 1]);
+  return FS_OK;
+}
+
+size_t online_bounds_workspace(int32_t V, int32_t n_chunks) {
+  return fs::round_up(sizeof(double) * V, 256) + fs::round_up(sizeof(double) * n_chunks, 256);
+}
+
+// fused partials for the longest chunk (at most V rows), then |h_b| (fp64),
+// final flags and one live count per chunk
+size_t online_workspace(int32_t B, int32_t V, int32_t n_chunks) {
+  return fused_workspace(B, V) + fs::round_up(sizeof(double) * B, 256) +
+         fs::round_up(sizeof(int32_t) * B, 256) + fs::round_up(sizeof(int32_t) * n_chunks, 256);
+}
+
 }  // namespace
 
 extern "C" {
@@ -226,6 +259,118 @@ fs_status fs_merge_lse(const float* partial_val, const int32_t* partial_idx,
                                              temperature, seed, step, out_ids, out_maxval,
                                              out_lse, static_cast<hipStream_t>(stream));
   if (e != hipSuccess) return hip_fail(e, "grouped merge launch");
+  return FS_OK;
+}
+
+size_t fs_online_bounds_workspace_bytes(int32_t V, int32_t n_chunks) {
+  if (V < 1 || n_chunks < 1 || n_chunks > kMaxChunks) return 0;
+  return online_bounds_workspace(V, n_chunks);
+}
+
+size_t fs_online_workspace_bytes(int32_t B, int32_t D, int32_t V, int32_t n_chunks) {
+  if (check_shape(B, D, V, 0) != FS_OK || n_chunks < 1 || n_chunks > kMaxChunks) return 0;
+  return online_workspace(B, V, n_chunks);
+}
+
+fs_status fs_online_bounds(const void* W, int32_t V, int32_t D, const int32_t* cuts,
+                           int32_t n_chunks, double* later_norm, void* workspace,
+                           size_t workspace_bytes, void* stream) {
+  fs_status s = check_shape(1, D, V, 0);
+  if (s != FS_OK) return s;
+  if ((s = check_cuts(cuts, n_chunks, V, "fs_online_bounds")) != FS_OK) return s;
+  if (!W || !later_norm || !workspace) return fail(FS_ERR_INVALID_ARG, "null pointer argument");
+  if (!aligned(W, 16)) return fail(FS_ERR_INVALID_ARG, "W must be 16-byte aligned");
+  if (!aligned(later_norm, 8)) return fail(FS_ERR_INVALID_ARG, "later_norm must be 8-byte aligned");
+  if (!aligned(workspace, 256)) return fail(FS_ERR_INVALID_ARG, "workspace must be 256-byte aligned");
+  const size_t need = online_bounds_workspace(V, n_chunks);
+  if (workspace_bytes < need)
+    return fail(FS_ERR_WORKSPACE, "fs_online_bounds: workspace of %zu bytes is below the %zu required",
+                workspace_bytes, need);
+  const hipStream_t st = static_cast<hipStream_t>(stream);
+  double* norms = static_cast<double*>(workspace);
+  double* chunk_max = reinterpret_cast<double*>(static_cast<char*>(workspace) +
+                                                fs::round_up(sizeof(double) * V, 256));
+  hipError_t e = fs::launch_row_norms(static_cast<const __bf16*>(W), V, D, norms, st);
+  if (e != hipSuccess) return hip_fail(e, "row norm launch");
+  for (int32_t c = 0; c < n_chunks; ++c) {
+    e = fs::launch_max_reduce(norms + cuts[c], cuts[c + 1] - cuts[c], chunk_max + c, st);
+    if (e != hipSuccess) return hip_fail(e, "chunk norm launch");
+  }
+  e = fs::launch_suffix_max(chunk_max, n_chunks, later_norm, st);
+  if (e != hipSuccess) return hip_fail(e, "suffix max launch");
+  return FS_OK;
+}
+
+fs_status fs_sample_online(const void* h, const void* W, int32_t B, int32_t D, int32_t V,
+                           int32_t vocab_offset, const float* temperature, uint64_t seed,
+                           uint64_t step, const int32_t* cuts, int32_t n_chunks,
+                           const double* later_norm, int32_t* out_ids, float* out_maxval,
+                           int32_t* out_chunks, void* workspace, size_t workspace_bytes,
+                           void* stream) {
+  const char* who = "fs_sample_online";
+  fs_status s = check_sample_args(h, W, B, D, V, vocab_offset, temperature, out_ids, out_maxval,
+                                  workspace);
+  if (s != FS_OK) return s;
+  if ((s = check_cuts(cuts, n_chunks, V, who)) != FS_OK) return s;
+  if (B == 0) return FS_OK;
+  if (!out_chunks || !later_norm) return fail(FS_ERR_INVALID_ARG, "null pointer argument");
+  if (!aligned(out_chunks, 4) || !aligned(later_norm, 8))
+    return fail(FS_ERR_INVALID_ARG, "out_chunks must be 4-byte and later_norm 8-byte aligned");
+  if (D > kMaxOnlineD)
+    return fail(FS_ERR_UNSUPPORTED, "%s: D=%d exceeds %d, where the bound's rounding margin holds",
+                who, D, kMaxOnlineD);
+  const size_t need = online_workspace(B, V, n_chunks);
+  if (workspace_bytes < need)
+    return fail(FS_ERR_WORKSPACE, "%s: workspace of %zu bytes is below the %zu required", who,
+                workspace_bytes, need);
+  // the chunks' configurations, checked before anything is launched
+  for (int32_t c = 0; c < n_chunks; ++c) {
+    const int cfg = choose_config(B, D, cuts[c + 1] - cuts[c]);
+    if (!fs::fused_config_supports(cfg, B, D))
+      return fail(FS_ERR_UNSUPPORTED, "%s: forced configuration %s does not support B=%d, D=%d",
+                  who, fs::fused_config_name(cfg), B, D);
+  }
+  const size_t S = max_splits(V);
+  const size_t region = fs::round_up(sizeof(float) * B * S, 256);
+  char* ws = static_cast<char*>(workspace);
+  float* part_val = reinterpret_cast<float*>(ws);
+  int32_t* part_idx = reinterpret_cast<int32_t*>(ws + region);
+  char* tail = ws + fused_workspace(B, V);
+  double* hnorm = reinterpret_cast<double*>(tail);
+  tail += fs::round_up(sizeof(double) * B, 256);
+  int32_t* done = reinterpret_cast<int32_t*>(tail);
+  tail += fs::round_up(sizeof(int32_t) * B, 256);
+  int32_t* live = reinterpret_cast<int32_t*>(tail);
+  // largest value of the Gumbel map on the uniform grid: u = 1 - 2^-24
+  const double g_max = -std::log(-std::log1p(-0x1p-24));
+  const double margin = 1.0 + 0x1p-8;
+  const hipStream_t st = static_cast<hipStream_t>(stream);
+  hipError_t e = fs::launch_online_init(static_cast<const __bf16*>(h), B, D, n_chunks, hnorm,
+                                        done, live, out_ids, out_maxval, out_chunks, st);
+  if (e != hipSuccess) return hip_fail(e, "online init launch");
+  for (int32_t c = 0; c < n_chunks; ++c) {
+    fs::SampleArgs a;
+    a.h = static_cast<const __bf16*>(h);
+    a.W = static_cast<const __bf16*>(W) + static_cast<size_t>(cuts[c]) * D;
+    a.B = B;
+    a.D = D;
+    a.V = cuts[c + 1] - cuts[c];
+    a.vocab_offset = vocab_offset + cuts[c];
+    a.temperature = temperature;
+    a.seed = seed;
+    a.step = step;
+    a.part_val = part_val;
+    a.part_idx = part_idx;
+    a.part_lse = nullptr;
+    a.S = 0;
+    a.live = c > 0 ? live + (c - 1) : nullptr;
+    e = fs::launch_fused(choose_config(B, D, a.V), a, st);
+    if (e != hipSuccess) return hip_fail(e, "fused sampler launch");
+    e = fs::launch_online_step(part_val, part_idx, a.S, B, c, n_chunks, later_norm, hnorm,
+                               temperature, g_max, margin, done, live, out_ids, out_maxval,
+                               out_chunks, st);
+    if (e != hipSuccess) return hip_fail(e, "online step launch");
+  }
   return FS_OK;
 }
 

@@ -18,6 +18,9 @@ struct SampleArgs {
   int32_t* part_idx;  // [B][S] their global ids
   float* part_lse;    // [B][S] per-block log-sum-exp of z / T (grouped sampler), or null
   int32_t S;          // number of vocabulary blocks (set by the launcher)
+  // If non-null and *live == 0 when a block starts, the block does nothing
+  // (the online sampler's later chunks, once every row is final).
+  const int32_t* live = nullptr;
 };
 
 // One fused-sampler configuration (a main-loop policy and its tile shape).
@@ -64,6 +67,28 @@ hipError_t launch_merge_groups_lse(const float* val, const int32_t* idx, const f
                                    int32_t P, int32_t B, const float* temperature,
                                    uint64_t seed, uint64_t step, int32_t* out_ids,
                                    float* out_val, float* out_lse, hipStream_t stream);
+
+// ---- online sampler with early finalisation (fs_online.hip) ----
+// Euclidean norm of each of the n rows of X (bf16, row length D), fp64.
+hipError_t launch_row_norms(const __bf16* X, int32_t n, int32_t D, double* out,
+                            hipStream_t stream);
+// out[0] = max of x[0 .. n).
+hipError_t launch_max_reduce(const double* x, int32_t n, double* out, hipStream_t stream);
+// later[c] = max(chunk_max[c+1 .. n_chunks)), later[n_chunks - 1] = 0.
+hipError_t launch_suffix_max(const double* chunk_max, int32_t n_chunks, double* later,
+                             hipStream_t stream);
+// Row norms of h, running pairs (-inf, INT32_MAX), done flags and live counts cleared.
+hipError_t launch_online_init(const __bf16* h, int32_t B, int32_t D, int32_t n_chunks,
+                              double* hnorm, int32_t* done, int32_t* live, int32_t* out_ids,
+                              float* out_val, int32_t* out_chunks, hipStream_t stream);
+// Chunk c of the online sampler: merges the chunk's S tile partials into the
+// running pair of every row not yet final, tests the bound and counts the
+// rows still live into live[c].  Does nothing if c > 0 and live[c-1] == 0.
+hipError_t launch_online_step(const float* part_val, const int32_t* part_idx, int32_t S,
+                              int32_t B, int32_t c, int32_t n_chunks, const double* later,
+                              const double* hnorm, const float* temperature, double g_max,
+                              double margin, int32_t* done, int32_t* live, int32_t* out_ids,
+                              float* out_val, int32_t* out_chunks, hipStream_t stream);
 
 hipError_t launch_debug_noise(uint64_t seed, uint64_t step, uint32_t row, uint32_t gv0,
                               int64_t n, uint32_t* bits, float* g, hipStream_t stream);

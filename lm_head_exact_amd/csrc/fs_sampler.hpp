@@ -81,6 +81,7 @@ __attribute__((amdgpu_waves_per_eu(Loop::kWavesPerSimd))) void fused_sample_kern
   int tile, bblock;
   block_tile<Loop>(a, tile, bblock);
   if (tile >= a.S) return;  // padding block of a paired grid (block-uniform)
+  if (a.live != nullptr && *a.live == 0) return;  // nothing left to sample (uniform)
   const int row0 = Loop::row0(tile, wave) - shift;
   const int block_col0 = bblock * Loop::kBlockCols;
 
@@ -205,6 +206,7 @@ __global__ __launch_bounds__(NW * kWave) void persist_sample_kernel(SampleArgs a
   static_assert(KS % P == 0, "the load ring must tile a group");
   extern __shared__ __attribute__((aligned(16))) unsigned char dyn_smem[];
   f32x4* red = reinterpret_cast<f32x4*>(dyn_smem);  // [2][NW][NT][kWave]
+  if (a.live != nullptr && *a.live == 0) return;  // nothing left to sample (uniform)
   const int lane = threadIdx.x & (kWave - 1);
   const int wave = threadIdx.x >> 6;
   const int li = lane & 15, kb = lane >> 4;

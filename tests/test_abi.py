@@ -157,3 +157,70 @@ def test_workspace_covers_the_shifted_grid(L):
     for V in (13, 16, 17, 1000, 16032):
         ws = L.fs_workspace_bytes(5, 256, V)
         assert ws >= 3 * 4 * 5 * ((V + 3 + 15) // 16)
+
+
+# ---- online sampler with early finalisation ----
+def _cuts(*c):
+    return (ctypes.c_int32 * len(c))(*c)
+
+
+def _online(L, h=ALIGNED, W=ALIGNED, B=4, D=256, V=1000, off=0, T=ALIGNED, cuts=None, n=2,
+            later=ALIGNED, ids=ALIGNED, val=ALIGNED, chunks=ALIGNED, ws=WS_ALIGNED,
+            wsb=1 << 30):
+    cuts = _cuts(0, 500, 1000) if cuts is None else cuts
+    return L.fs_sample_online(h, W, B, D, V, off, T, 1, 2, cuts, n, later, ids, val, chunks, ws,
+                              wsb, None)
+
+
+@pytest.mark.parametrize("kw,status", [
+    (dict(cuts=_cuts(0, 500, 999)), bd.FS_ERR_INVALID_ARG),        # does not end at V
+    (dict(cuts=_cuts(1, 500, 1000)), bd.FS_ERR_INVALID_ARG),       # does not start at 0
+    (dict(cuts=_cuts(0, 600, 600, 1000), n=3), bd.FS_ERR_INVALID_ARG),  # empty chunk
+    (dict(cuts=_cuts(0, 700, 300, 1000), n=3), bd.FS_ERR_INVALID_ARG),  # decreasing
+    (dict(n=0), bd.FS_ERR_INVALID_ARG),
+    (dict(n=70000), bd.FS_ERR_INVALID_ARG),
+    (dict(later=None), bd.FS_ERR_INVALID_ARG),
+    (dict(later=ALIGNED + 4), bd.FS_ERR_INVALID_ARG),
+    (dict(chunks=None), bd.FS_ERR_INVALID_ARG),
+    (dict(chunks=ALIGNED + 2), bd.FS_ERR_INVALID_ARG),
+    (dict(D=7), bd.FS_ERR_INVALID_ARG),
+    (dict(h=None), bd.FS_ERR_INVALID_ARG),
+    (dict(W=ALIGNED + 8), bd.FS_ERR_INVALID_ARG),
+    (dict(D=32776, cuts=_cuts(0, 500, 1000)), bd.FS_ERR_UNSUPPORTED),
+    (dict(wsb=16), bd.FS_ERR_WORKSPACE),
+    (dict(B=0, h=None, W=None, T=None, later=None, ids=None, val=None, chunks=None, ws=None),
+     bd.FS_OK),
+])
+def test_online_argument_errors(L, kw, status):
+    assert _online(L, **kw) == status
+    if status != bd.FS_OK:
+        assert len(L.fs_last_error()) > 0
+
+
+def test_online_workspace_sizes(L):
+    assert L.fs_online_workspace_bytes(4, 7, 1000, 2) == 0
+    assert L.fs_online_workspace_bytes(4, 256, 1000, 0) == 0
+    need = L.fs_online_workspace_bytes(4, 256, 1000, 2)
+    assert need >= L.fs_workspace_bytes(4, 256, 1000) + 4 * (8 + 4) + 2 * 4
+    assert need % 256 == 0
+    assert _online(L, wsb=need - 1) == bd.FS_ERR_WORKSPACE
+    assert _online(L, wsb=need, ws=WS_ALIGNED + 4) == bd.FS_ERR_INVALID_ARG
+    assert L.fs_online_bounds_workspace_bytes(0, 2) == 0
+    assert L.fs_online_bounds_workspace_bytes(1000, 2) >= 8 * 1000 + 8 * 2
+
+
+def test_online_bounds_argument_errors(L):
+    c = _cuts(0, 500, 1000)
+    ok = dict(W=ALIGNED, V=1000, D=256, cuts=c, n=2, later=ALIGNED, ws=WS_ALIGNED, wsb=1 << 30)
+
+    def call(**kw):
+        a = {**ok, **kw}
+        return L.fs_online_bounds(a["W"], a["V"], a["D"], a["cuts"], a["n"], a["later"], a["ws"],
+                                  a["wsb"], None)
+    assert call(cuts=_cuts(0, 500, 900)) == bd.FS_ERR_INVALID_ARG
+    assert call(W=None) == bd.FS_ERR_INVALID_ARG
+    assert call(W=ALIGNED + 2) == bd.FS_ERR_INVALID_ARG
+    assert call(later=ALIGNED + 4) == bd.FS_ERR_INVALID_ARG
+    assert call(D=12) == bd.FS_ERR_INVALID_ARG
+    assert call(ws=WS_ALIGNED + 8) == bd.FS_ERR_INVALID_ARG
+    assert call(wsb=8) == bd.FS_ERR_WORKSPACE

@@ -42,11 +42,21 @@ def _demangle(names):
     return r.stdout.splitlines()
 
 
+ALL_UNITS = tuple(sorted(f for f in os.listdir(CSRC) if f.endswith(".hip")))
+
+
 @pytest.fixture(scope="module")
-def dma_kernels(tmp_path_factory):
+def assembly(tmp_path_factory):
+    """gfx950 assembly of every translation unit of the library, by name."""
     outdir = str(tmp_path_factory.mktemp("asm"))
-    with ThreadPoolExecutor(len(DMA_UNITS)) as ex:
-        texts = list(ex.map(lambda u: _assemble(u, outdir), DMA_UNITS))
+    with ThreadPoolExecutor(4) as ex:
+        texts = list(ex.map(lambda u: _assemble(u, outdir), ALL_UNITS))
+    return dict(zip(ALL_UNITS, texts))
+
+
+@pytest.fixture(scope="module")
+def dma_kernels(assembly):
+    texts = [assembly[u] for u in DMA_UNITS]
     kernels = {}
     for s in texts:
         names = re.findall(r"^(_Z\S*fused_sample_kernel\S*):", s, re.M)
@@ -103,3 +113,14 @@ def test_dma_every_barrier_follows_a_vector_memory_wait(dma_kernels):
                 waited = False
             prev = t
         assert seen >= 2, f"{name}: staging barriers not found ({seen})"
+
+
+def test_no_scalar_memory_writes(assembly):
+    """No device code of the library writes through the scalar data cache
+    (scalar stores, scalar atomics, its write-back or discard): every store
+    and atomic is a vector-memory instruction."""
+    pat = re.compile(r"^\s*s_(store|atomic|buffer_store|buffer_atomic|scratch_store|dcache_wb|"
+                     r"dcache_discard)\w*", re.M)
+    for unit, s in assembly.items():
+        hits = pat.findall(s)
+        assert not hits, f"{unit}: scalar memory writes {hits[:4]}"
