@@ -8,14 +8,16 @@ already resident in device memory and a fresh (seed, step) per step.  The
 headline line is B = 32; the same line carries the B = 1 .. 256 sweep, the
 unfused baseline (logits and probabilities through device memory) timed the
 same way, the grouped (hierarchical) sampler over 1 and 8 vocabulary groups,
-the online sampler with early finalisation (8 vocabulary chunks), the
+the online sampler with early finalisation (8 vocabulary chunks), the packed
+(fragment-order) weight path beside each row-major figure, the
 Qwen3-shaped, large-batch and vocabulary-shard heads, the fused kernel's
 roofline fraction and the CPU oracle's rate.
 
 Prints ONE JSON line on stdout.  Usage:
   python bench.py [--gpus 1] [--steps K] [--warmup W] [--batch 32]
                   [--sweep 1,2,4,...] [--no-cpu-baseline] [--no-unfused]
-                  [--no-grouped] [--no-online] [--no-workloads] [--profile-pass]
+                  [--no-grouped] [--no-online] [--no-packed] [--no-workloads]
+                  [--profile-pass]
 --profile-pass runs a short fixed sequence for rocprofv3 (a few fused steps
 plus a 1 GiB device copy used to calibrate the HBM byte counters) and exits.
 """
@@ -47,6 +49,7 @@ def parse():
     ap.add_argument("--no-grouped", action="store_true")
     ap.add_argument("--no-workloads", action="store_true")
     ap.add_argument("--no-online", action="store_true")
+    ap.add_argument("--no-packed", action="store_true")
     ap.add_argument("--profile-pass", action="store_true")
     return ap.parse_args()
 
@@ -157,7 +160,10 @@ def main():
     W = wl.make_w(wlk, dev)
     stream = torch.cuda.current_stream(dev)
 
-    def make_step(B, unfused=False):
+    # W in fragment order (packed once, as at model load) for fs_sample_packed
+    Wp = fsl.pack_weights(W) if not (args.no_packed or args.profile_pass) else None
+
+    def make_step(B, unfused=False, packed=False):
         h = wl.make_h(wlk, B, dev)
         T = wl.make_temperature(wlk, B, dev)
         out = (torch.empty(B, dtype=torch.int32, device=dev),
@@ -171,7 +177,10 @@ def main():
 
         def fn(i):
             seed, step = wlk.sampler_seed(i)
-            call(h, W, T, seed, step, out=out, workspace=ws)
+            if packed:
+                fsl.sample_packed(h, Wp, V, T, seed, step, out=out, workspace=ws)
+            else:
+                call(h, W, T, seed, step, out=out, workspace=ws)
         return fn, (h, T, out, ws)
 
     if args.profile_pass:
@@ -207,6 +216,15 @@ def main():
                  "kernel_hbm_GBs": round(algorithmic_bytes(b, D, V) / (kt * 1e3), 1),
                  "kernel_mfma_TFLOPs": round(flops(b, D, V) / (kt * 1e6), 1),
                  "tokens_per_s": round(b / (t * 1e-6), 1)}
+        if Wp is not None:
+            pf, pkp = make_step(b, packed=True)
+            pt = time_steps(torch, pf, args.sweep_steps, 10, stream) * 1e3
+            pkt, _, _, _ = measure_fused_kernel(torch, fsl, pf, args.sweep_steps, 5)
+            entry["packed_config"] = fsl.config_name(fsl.selected_config(b, D, V, packed=True))
+            entry["packed_us_per_step"] = round(pt, 2)
+            entry["packed_kernel_us"] = round(pkt * 1e3, 2)
+            entry["packed_frac_of_roofline"] = round(roofline_us(b, D, V) / pt, 4)
+            del pkp
         if not args.no_unfused:
             uf, ukp = make_step(b, unfused=True)
             ut = time_steps(torch, uf, max(10, args.sweep_steps // 4), 3, stream) * 1e3
@@ -321,6 +339,7 @@ def main():
         for wk, Bs, copies in ((wl.QWEN3, (64, 128, 256), 1), (wl.LARGE_BATCH, (256, 512), 1),
                                (wl.TP8_SHARD, (1, 64, 256), 4)):
             Ws = [wl.make_w(wk, dev) for _ in range(copies)]
+            Wps = [fsl.pack_weights(x, wk.vocab_offset) for x in Ws] if not args.no_packed else []
             for b in Bs:
                 h_w = wl.make_h(wk, b, dev)
                 T_w = wl.make_temperature(wk, b, dev)
@@ -345,9 +364,18 @@ def main():
                                     5, stream) * 1e3
                     e["w_copies_rotated"] = copies
                     e["hot_us_per_step"] = round(th, 2)
+                if Wps:
+                    def pfn(i, Wps=Wps, h_w=h_w, T_w=T_w, out_w=out_w, ws_w=ws_w, wk=wk):
+                        seed, step = wk.sampler_seed(i)
+                        fsl.sample_packed(h_w, Wps[i % len(Wps)], wk.V, T_w, seed, step,
+                                          vocab_offset=wk.vocab_offset, out=out_w, workspace=ws_w)
+                    tp = time_steps(torch, pfn, max(20, args.sweep_steps // 2), 5, stream) * 1e3
+                    e["packed_config"] = fsl.config_name(fsl.selected_config(b, wk.D, wk.V, packed=True))
+                    e["packed_us_per_step"] = round(tp, 2)
+                    e["packed_frac_of_roofline"] = round(roof / tp, 4)
                 workloads.append(e)
                 del h_w, T_w, out_w, ws_w
-            del Ws
+            del Ws, Wps
             torch.cuda.empty_cache()
 
     unf_us = None

@@ -91,6 +91,39 @@ FS_API fs_status fs_sample(const void* h, const void* W, int32_t B, int32_t D, i
                     uint64_t step, int32_t* out_ids, float* out_maxval,
                     void* workspace, size_t workspace_bytes, void* stream);
 
+/* Fragment-order weights.  The sampler reads W one MFMA operand fragment at
+ * a time (16 vocabulary rows x 32 k, 16 bytes per lane); from row-major W
+ * each such read takes 64 bytes from each of 16 rows 8 KB apart, which costs
+ * HBM page locality.  fs_pack_weights copies W once (at model load) into the
+ * fragment order the kernels consume: the vocabulary rows in groups of 16
+ * starting at row -(vocab_offset mod 4), each group stored k-step by k-step
+ * as 64 pieces of 16 bytes (element ((g * D/32 + s) * 64 + l) * 8 + j holds
+ * W[16 g + (l mod 16) - (vocab_offset mod 4)][32 s + 8 (l / 16) + j], zero
+ * outside [0, V)).
+ *   W            bf16 [V][D], device, 16-byte aligned; D % 32 == 0
+ *   vocab_offset the offset the packed weights will be sampled at (only its
+ *                value mod 4 shapes the layout)
+ *   W_packed     device, 16-byte aligned, >= fs_packed_weights_bytes(V, D,
+ *                vocab_offset) bytes (0 for invalid arguments); caller-owned
+ * fs_sample_packed takes fs_sample's arguments with W_packed in place of W
+ * (packed for the same V, D and vocab_offset mod 4).  Its kernels read the
+ * same operand fragments as fs_sample's: run in one configuration
+ * (fs_force_config) the two return the same ids and scores bit for bit; the
+ * automatic choices may differ (fs_selected_config_packed), and then so may
+ * the scores' last bits, within the parity bound of fs_sample.  It runs the
+ * persistent, DMA-staged and LDS-staged kernels; a shape whose configuration
+ * has no fragment-order kernel (the K-split and streaming loops chosen for
+ * small batches at unusual D) returns FS_ERR_UNSUPPORTED.  D % 32 != 0 is
+ * FS_ERR_INVALID_ARG. */
+FS_API size_t fs_packed_weights_bytes(int32_t V, int32_t D, int32_t vocab_offset);
+FS_API fs_status fs_pack_weights(const void* W, int32_t V, int32_t D, int32_t vocab_offset,
+                                 void* W_packed, size_t packed_bytes, void* stream);
+FS_API fs_status fs_sample_packed(const void* h, const void* W_packed, int32_t B, int32_t D,
+                                  int32_t V, int32_t vocab_offset, const float* temperature,
+                                  uint64_t seed, uint64_t step, int32_t* out_ids,
+                                  float* out_maxval, void* workspace, size_t workspace_bytes,
+                                  void* stream);
+
 /* One vocabulary shard's contribution for the grouped / tensor-parallel flow
  * (wiki summary, "Method": each rank reduces its own shard to a per-row
  * (local max, local argmax) pair, and only those pairs are exchanged).
@@ -229,8 +262,10 @@ FS_API fs_status fs_debug_gumbel(const uint32_t* bits, int64_t n, float* out_gum
 FS_API int32_t fs_num_configs(void);
 FS_API const char* fs_config_name(int32_t id);
 FS_API fs_status fs_force_config(int32_t id);
-/* Configuration fs_sample would use for batch size B (after forcing). */
+/* Configuration fs_sample would use for batch size B (after forcing), and
+ * the one fs_sample_packed would use. */
 FS_API int32_t fs_selected_config(int32_t B, int32_t D, int32_t V);
+FS_API int32_t fs_selected_config_packed(int32_t B, int32_t D, int32_t V);
 
 /* Profiling of the fused kernel.  fs_profile_enable(capacity) creates
  * 2 * capacity HIP events (outside any sampling call); while enabled, each of

@@ -10,7 +10,8 @@ _BINDING_NAMES = ("sample", "sample_partial", "merge", "sample_partial_lse", "me
                   "unfused_workspace_bytes", "library_path", "debug_noise", "debug_gumbel",
                   "num_configs", "config_name", "profile_enable", "profile_read", "force_config", "selected_config",
                   "FlashSampleError", "alloc_workspace", "online_bounds", "sample_online",
-                  "online_workspace_bytes")
+                  "online_workspace_bytes", "pack_weights", "sample_packed",
+                  "packed_weights_bytes")
 __all__ = list(_BINDING_NAMES)
 
 

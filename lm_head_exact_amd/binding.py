@@ -61,6 +61,9 @@ def lib():
         ("fs_sample_partial_lse", [vp, vp, i32, i32, i32, i32, vp, u64, u64, vp, vp, vp, vp,
                                    sz, vp], ctypes.c_int),
         ("fs_merge_lse", [vp, vp, vp, i32, i32, vp, u64, u64, vp, vp, vp, vp], ctypes.c_int),
+        ("fs_packed_weights_bytes", [i32, i32, i32], sz),
+        ("fs_pack_weights", [vp, i32, i32, i32, vp, sz, vp], ctypes.c_int),
+        ("fs_sample_packed", sample_args, ctypes.c_int),
         ("fs_online_bounds_workspace_bytes", [i32, i32], sz),
         ("fs_online_workspace_bytes", [i32, i32, i32, i32], sz),
         ("fs_online_bounds", [vp, i32, i32, vp, i32, vp, vp, sz, vp], ctypes.c_int),
@@ -72,6 +75,7 @@ def lib():
         ("fs_config_name", [i32], ctypes.c_char_p),
         ("fs_force_config", [i32], ctypes.c_int),
         ("fs_selected_config", [i32, i32, i32], i32),
+        ("fs_selected_config_packed", [i32, i32, i32], i32),
         ("fs_profile_enable", [i32], ctypes.c_int),
         ("fs_profile_read", [ctypes.POINTER(ctypes.c_int32)] + [ctypes.POINTER(ctypes.c_double)] * 3,
          ctypes.c_int),
@@ -261,6 +265,53 @@ def merge(partial_val: torch.Tensor, partial_idx: torch.Tensor, out=None):
     return ids, val
 
 
+def packed_weights_bytes(V: int, D: int, vocab_offset: int = 0) -> int:
+    return int(lib().fs_packed_weights_bytes(V, D, vocab_offset))
+
+
+def pack_weights(W: torch.Tensor, vocab_offset: int = 0) -> torch.Tensor:
+    """W (V x D bf16) in the kernels' fragment order, as a flat bf16 tensor;
+    sample it with sample_packed at the same vocab_offset (mod 4)."""
+    _req(W, "W", torch.bfloat16, 2)
+    V, D = W.shape
+    n = packed_weights_bytes(V, D, vocab_offset)
+    if n == 0:
+        raise FlashSampleError(FS_ERR_INVALID_ARG, f"cannot pack a {V} x {D} W (D % 32 != 0?)")
+    Wp = torch.empty(n // 2, dtype=torch.bfloat16, device=W.device)
+    _check(lib().fs_pack_weights(_ptr(W), V, D, int(vocab_offset), _ptr(Wp), n,
+                                 _stream(W.device)))
+    return Wp
+
+
+def sample_packed(h: torch.Tensor, W_packed: torch.Tensor, V: int, temperature: torch.Tensor,
+                  seed: int, step: int, vocab_offset: int = 0, out=None, workspace=None):
+    """fs_sample on fragment-order weights (pack_weights): returns (ids, maxval),
+    identical to sample() on the row-major W."""
+    _req(h, "h", torch.bfloat16, 2)
+    _req(W_packed, "W_packed", torch.bfloat16, 1)
+    _req(temperature, "temperature", torch.float32, 1)
+    B, D = h.shape
+    need = packed_weights_bytes(V, D, vocab_offset)
+    if need == 0 or W_packed.numel() * 2 < need:
+        raise ValueError(f"W_packed holds {W_packed.numel() * 2} bytes; {need} needed")
+    if temperature.shape[0] != B:
+        raise ValueError("temperature must have B entries")
+    dev = h.device
+    if out is None:
+        out = (torch.empty(B, dtype=torch.int32, device=dev),
+               torch.empty(B, dtype=torch.float32, device=dev))
+    ids, val = out
+    if len({t.device for t in (h, W_packed, temperature, ids, val)}) != 1:
+        raise ValueError("all tensors must be on one device")
+    if workspace is None:
+        workspace = alloc_workspace(workspace_bytes(B, D, V), dev)
+    _check(lib().fs_sample_packed(_ptr(h), _ptr(W_packed), B, D, V, int(vocab_offset),
+                                  _ptr(temperature), int(seed) & (2**64 - 1),
+                                  int(step) & (2**64 - 1), _ptr(ids), _ptr(val), _ptr(workspace),
+                                  workspace.numel() * workspace.element_size(), _stream(dev)))
+    return ids, val
+
+
 def _host_cuts(cuts):
     """cuts as a host int32 ctypes array (kept alive by the caller) and the chunk count."""
     c = [int(x) for x in (cuts.tolist() if hasattr(cuts, "tolist") else cuts)]
@@ -366,5 +417,7 @@ def force_config(i: int):
     _check(lib().fs_force_config(int(i)))
 
 
-def selected_config(B: int, D: int, V: int) -> int:
-    return int(lib().fs_selected_config(B, D, V))
+def selected_config(B: int, D: int, V: int, packed: bool = False) -> int:
+    """Configuration fs_sample (packed: fs_sample_packed) would use."""
+    fn = lib().fs_selected_config_packed if packed else lib().fs_selected_config
+    return int(fn(B, D, V))

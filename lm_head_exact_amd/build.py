@@ -16,7 +16,7 @@ BUILD = os.path.join(ROOT, "_build")
 LIB = os.path.join(HERE, "libflashsample.so")
 SOURCES = ["fs_configs_dma_a.hip", "fs_configs_dma_b.hip", "fs_configs_lds.hip",
            "fs_configs_small.hip", "fs_fused.hip", "fs_api.hip", "fs_unfused.hip",
-           "fs_online.hip"]
+           "fs_online.hip", "fs_pack.hip"]
 
 HIPCC = os.environ.get("HIPCC", "/opt/rocm/bin/hipcc")
 ARCH = "gfx950"

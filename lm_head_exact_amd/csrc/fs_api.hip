@@ -96,9 +96,9 @@ void destroy_events() {
   g_prof.used = 0;
 }
 
-int choose_config(int32_t B, int32_t D, int32_t V) {
+int choose_config(int32_t B, int32_t D, int32_t V, bool packed = false) {
   const int forced = g_forced_config.load(std::memory_order_relaxed);
-  return forced >= 0 ? forced : fs::fused_auto_config(B, D, V);
+  return forced >= 0 ? forced : fs::fused_auto_config(B, D, V, packed);
 }
 
 // Shared body of fs_sample / fs_sample_partial / fs_sample_partial_lse
@@ -106,7 +106,8 @@ int choose_config(int32_t B, int32_t D, int32_t V) {
 fs_status run_fused(const void* h, const void* W, int32_t B, int32_t D, int32_t V,
                     int32_t vocab_offset, const float* temperature, uint64_t seed,
                     uint64_t step, int32_t* out_ids, float* out_val, float* out_lse,
-                    void* workspace, size_t workspace_bytes, void* stream, const char* who) {
+                    void* workspace, size_t workspace_bytes, void* stream, const char* who,
+                    bool w_packed = false) {
   if (out_lse && !aligned(out_lse, 4))
     return fail(FS_ERR_INVALID_ARG, "%s: partial_lse must be 4-byte aligned", who);
   fs_status s = check_sample_args(h, W, B, D, V, vocab_offset, temperature, out_ids, out_val,
@@ -116,10 +117,15 @@ fs_status run_fused(const void* h, const void* W, int32_t B, int32_t D, int32_t 
   if (workspace_bytes < need)
     return fail(FS_ERR_WORKSPACE, "%s: workspace of %zu bytes is below the %zu required", who,
                 workspace_bytes, need);
-  const int cfg = choose_config(B, D, V);
+  if (w_packed && D % 32 != 0)
+    return fail(FS_ERR_INVALID_ARG, "%s: D must be a multiple of 32 (got %d)", who, D);
+  const int cfg = choose_config(B, D, V, w_packed);
   if (!fs::fused_config_supports(cfg, B, D))
     return fail(FS_ERR_UNSUPPORTED, "%s: forced configuration %s does not support B=%d, D=%d",
                 who, fs::fused_config_name(cfg), B, D);
+  if (w_packed && !fs::fused_config_reads_packed(cfg))
+    return fail(FS_ERR_UNSUPPORTED, "%s: configuration %s for B=%d, D=%d, V=%d has no packed-W kernel",
+                who, fs::fused_config_name(cfg), B, D, V);
   const size_t S = max_splits(V);
   fs::SampleArgs a;
   a.h = static_cast<const __bf16*>(h);
@@ -137,6 +143,7 @@ fs_status run_fused(const void* h, const void* W, int32_t B, int32_t D, int32_t 
   a.part_lse = out_lse ? reinterpret_cast<float*>(static_cast<char*>(workspace) + 2 * region)
                        : nullptr;
   a.S = 0;
+  a.w_packed = w_packed;
   const hipStream_t st = static_cast<hipStream_t>(stream);
   hipError_t e;
   if (g_prof.on.load(std::memory_order_acquire)) {
@@ -218,6 +225,40 @@ fs_status fs_sample(const void* h, const void* W, int32_t B, int32_t D, int32_t 
                     size_t workspace_bytes, void* stream) {
   return run_fused(h, W, B, D, V, vocab_offset, temperature, seed, step, out_ids, out_maxval,
                    nullptr, workspace, workspace_bytes, stream, "fs_sample");
+}
+
+size_t fs_packed_weights_bytes(int32_t V, int32_t D, int32_t vocab_offset) {
+  if (check_shape(1, D, V, vocab_offset) != FS_OK || D % 32 != 0) return 0;
+  return static_cast<size_t>(fs::packed_groups(V, vocab_offset)) * 16 * D * sizeof(uint16_t);
+}
+
+fs_status fs_pack_weights(const void* W, int32_t V, int32_t D, int32_t vocab_offset,
+                          void* W_packed, size_t packed_bytes, void* stream) {
+  fs_status s = check_shape(1, D, V, vocab_offset);
+  if (s != FS_OK) return s;
+  if (D % 32 != 0)
+    return fail(FS_ERR_INVALID_ARG, "fs_pack_weights: D must be a multiple of 32 (got %d)", D);
+  if (!W || !W_packed) return fail(FS_ERR_INVALID_ARG, "null pointer argument");
+  if (!aligned(W, 16) || !aligned(W_packed, 16))
+    return fail(FS_ERR_INVALID_ARG, "W and W_packed must be 16-byte aligned");
+  const size_t need = fs_packed_weights_bytes(V, D, vocab_offset);
+  if (packed_bytes < need)
+    return fail(FS_ERR_WORKSPACE, "fs_pack_weights: %zu bytes for W_packed, %zu required",
+                packed_bytes, need);
+  hipError_t e = fs::launch_pack_weights(static_cast<const __bf16*>(W), V, D, vocab_offset,
+                                         static_cast<__bf16*>(W_packed),
+                                         static_cast<hipStream_t>(stream));
+  if (e != hipSuccess) return hip_fail(e, "pack launch");
+  return FS_OK;
+}
+
+fs_status fs_sample_packed(const void* h, const void* W_packed, int32_t B, int32_t D, int32_t V,
+                           int32_t vocab_offset, const float* temperature, uint64_t seed,
+                           uint64_t step, int32_t* out_ids, float* out_maxval, void* workspace,
+                           size_t workspace_bytes, void* stream) {
+  return run_fused(h, W_packed, B, D, V, vocab_offset, temperature, seed, step, out_ids,
+                   out_maxval, nullptr, workspace, workspace_bytes, stream, "fs_sample_packed",
+                   true);
 }
 
 fs_status fs_sample_partial(const void* h, const void* W, int32_t B, int32_t D, int32_t V,
@@ -504,6 +545,11 @@ fs_status fs_force_config(int32_t id) {
 int32_t fs_selected_config(int32_t B, int32_t D, int32_t V) {
   if (check_shape(B, D, V, 0) != FS_OK) return -1;
   return choose_config(B, D, V);
+}
+
+int32_t fs_selected_config_packed(int32_t B, int32_t D, int32_t V) {
+  if (check_shape(B, D, V, 0) != FS_OK) return -1;
+  return choose_config(B, D, V, true);
 }
 
 const char* fs_status_string(fs_status s) {

@@ -18,6 +18,7 @@ int fused_configs_dma_b(const FusedConfig** out) {
       FS_DMAG(1, 4, 4, 64, 8, 3, 4, 2),
       FS_DMAG(1, 16, 4, 64, 8, 3, 4, 2),
       FS_DMAG(1, 8, 4, 64, 8, 3, 4, 2),
+      FS_DMAW(8, 4, 8, 64, 2, 3, 4, 2, 2),  // two batch groups of waves (WB = 2)
   };
   *out = k;
   return static_cast<int>(sizeof(k) / sizeof(k[0]));

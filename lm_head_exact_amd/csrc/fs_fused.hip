@@ -174,6 +174,10 @@ int fused_config_order(int id) {
   return (id >= 0 && id < num_fused_configs()) ? configs()[id].order : -1;
 }
 
+bool fused_config_reads_packed(int id) {
+  return id >= 0 && id < num_fused_configs() && configs()[id].packed_w;
+}
+
 bool fused_config_supports(int id, int32_t B, int32_t D) {
   return id >= 0 && id < num_fused_configs() && configs()[id].supports(B, D);
 }
@@ -206,7 +210,7 @@ double one_per_cu_fill(int id, int32_t V) {
 }
 }  // namespace
 
-int fused_auto_config(int32_t B, int32_t D, int32_t V) {
+int fused_auto_config(int32_t B, int32_t D, int32_t V, bool packed) {
   static const int persist[] = {config_id("persist_nt1_nw8_ks16_p8"),
                                 config_id("persist_nt2_nw8_ks16_p8"),
                                 config_id("persist_nt1_nw8_ks32_p8")};
@@ -233,7 +237,8 @@ int fused_auto_config(int32_t B, int32_t D, int32_t V) {
   static const int stream_big = config_id("stream_mr2_nt4_nw4_p4_ntl0");
   for (int id : persist)
     if (fused_config_supports(id, B, D)) return id;
-  if (B <= 8 && fused_config_supports(ksplit, B, D)) return ksplit;
+  // (the K-split loop reads row-major W only: packed W goes on to the DMA loop)
+  if (!packed && B <= 8 && fused_config_supports(ksplit, B, D)) return ksplit;
   // DMA candidates per batch width, first choice first: 512-row blocks, else
   // 640-row blocks where those fill the CUs better (a vocabulary of ~152k
   // rows gives 297 blocks of 512, two rounds on 256 CUs, but 238 of 640).
@@ -246,10 +251,17 @@ int fused_auto_config(int32_t B, int32_t D, int32_t V) {
   // Every candidate sums each logit's products in k order in one wave, like
   // the LDS loops below: the choice may depend on V, so a vocabulary shard
   // gets the same bits as the same rows inside a whole-vocabulary call.
+  //
+  // On fragment-order (packed) W the 640-row blocks come first up to 128
+  // batch rows whenever they fill the CUs (Llama-3 head: 182 against 217 us
+  // at B = 64, 193 against 222 us at B = 128): each wave then streams five
+  // contiguous 16-row groups.
   struct Pick { int dma[2]; int dma_short; int lds; };
   const int dma256_first = D <= 4096 ? dma256 : dma256_kc128;
-  const Pick p = B <= 64    ? Pick{{dma64, dma64_tall}, dma64_short, lds64}
-                 : B <= 128 ? Pick{{dma128, dma128_tall}, dma128_short, lds128}
+  const Pick p = B <= 64    ? (packed ? Pick{{dma64_tall, dma64}, dma64_short, lds64}
+                                      : Pick{{dma64, dma64_tall}, dma64_short, lds64})
+                 : B <= 128 ? (packed ? Pick{{dma128_tall, dma128}, dma128_short, lds128}
+                                      : Pick{{dma128, dma128_tall}, dma128_short, lds128})
                  : B <= 256 ? Pick{{dma256_first, dma256}, dma256_short, lds256}
                             : Pick{{dma_paired, dma256_first}, dma256_short, lds256};
   // below three quarters of the CUs busy on average over the rounds the LDS

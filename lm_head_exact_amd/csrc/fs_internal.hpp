@@ -21,6 +21,8 @@ struct SampleArgs {
   // If non-null and *live == 0 when a block starts, the block does nothing
   // (the online sampler's later chunks, once every row is final).
   const int32_t* live = nullptr;
+  // W in fragment order (fs_pack_weights) instead of row-major [V][D]
+  bool w_packed = false;
 };
 
 // One fused-sampler configuration (a main-loop policy and its tile shape).
@@ -30,6 +32,7 @@ struct FusedConfig {
   hipError_t (*launch)(SampleArgs&, hipStream_t);
   bool (*supports)(int32_t B, int32_t D);
   int order;  // configurations of equal order sum the contraction identically
+  bool packed_w;  // can read W in fragment order
 };
 
 // Configuration lists of the translation units fs_configs_*.hip.
@@ -42,8 +45,10 @@ int fused_configs_dma_b(const FusedConfig** out);
 int num_fused_configs();
 const char* fused_config_name(int id);
 int fused_rows_per_block(int id);
-int fused_auto_config(int32_t B, int32_t D, int32_t V);
+// Automatic choice; `packed`: for W in fragment order (fs_pack_weights).
+int fused_auto_config(int32_t B, int32_t D, int32_t V, bool packed = false);
 bool fused_config_supports(int id, int32_t B, int32_t D);
+bool fused_config_reads_packed(int id);
 // Configurations with equal order sum each logit's products identically.
 int fused_config_order(int id);
 // Smallest rows-per-block over all configurations: bounds the split count.
@@ -89,6 +94,14 @@ hipError_t launch_online_step(const float* part_val, const int32_t* part_idx, in
                               const double* hnorm, const float* temperature, double g_max,
                               double margin, int32_t* done, int32_t* live, int32_t* out_ids,
                               float* out_val, int32_t* out_chunks, hipStream_t stream);
+
+// ---- fragment-order W (fs_pack.hip) ----
+// Groups of 16 rows of the grid shifted by vocab_offset mod 4.
+inline int64_t packed_groups(int32_t V, int32_t vocab_offset) {
+  return (static_cast<int64_t>(V) + (vocab_offset & 3) + 15) / 16;
+}
+hipError_t launch_pack_weights(const __bf16* W, int32_t V, int32_t D, int32_t vocab_offset,
+                               __bf16* Wp, hipStream_t stream);
 
 hipError_t launch_debug_noise(uint64_t seed, uint64_t step, uint32_t row, uint32_t gv0,
                               int64_t n, uint32_t* bits, float* g, hipStream_t stream);

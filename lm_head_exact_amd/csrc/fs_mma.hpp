@@ -49,6 +49,21 @@ __device__ __forceinline__ bf16x8 load_frag(const __bf16* p) {
   return __builtin_bit_cast(bf16x8, NTL ? __builtin_nontemporal_load(q) : *q);
 }
 
+// Packed W (fragment order).  The vocabulary grid's 16-row groups are stored
+// one after another, each k-step by k-step as the 64 lanes' 16-byte A-fragment
+// pieces: element ((g * (D / 32) + s) * 64 + l) * 8 + j holds
+// W[16 g + (l % 16) - shift][32 s + 8 (l / 16) + j], zero for rows outside
+// [0, V), with shift = vocab_offset mod 4 (the grid's alignment of global ids).
+// A fragment load then reads 1 KB contiguous and a group's k-steps follow one
+// another in memory, so each wave streams its groups front to back instead of
+// taking 64 bytes from each of 16 rows 8 KB apart (HBM page locality).
+constexpr int kPackedStep = kWave * 8;  // elements from one k-step of a group to the next
+
+// The lane's piece of k-step 0 of group g.
+__device__ __forceinline__ const __bf16* packed_frag(const __bf16* Wp, int g, int32_t D, int lane) {
+  return Wp + (static_cast<size_t>(g) * (D / 32) * kWave + lane) * 8;
+}
+
 __device__ __forceinline__ bf16x8 zero_frag() {
   return __builtin_bit_cast(bf16x8, u32x4{0u, 0u, 0u, 0u});
 }
@@ -295,6 +310,10 @@ struct LdsLoop {
     });
   }
 
+  // PACKED: W is in fragment order (packed_frag), row0 is the wave's first
+  // grid row (a multiple of 16, not shifted) and V the number of groups.
+  static constexpr bool kPackedW = true;
+  template <bool PACKED = false>
   __device__ __forceinline__ static void run(const __bf16* __restrict__ W,
                                              const __bf16* __restrict__ h, int32_t B, int32_t D,
                                              int32_t V, int32_t row0, int32_t col0,
@@ -302,9 +321,13 @@ struct LdsLoop {
     const int lane = threadIdx.x & (kWave - 1);
     const int li = lane & 15, kb = lane >> 4;
     __bf16* hs = static_cast<__bf16*>(smem);
+    constexpr int kStep = PACKED ? kPackedStep : 32;  // elements between k-steps
     const __bf16* arow[MR];
     static_for<MR>([&](auto m) FS_INLINE {
-      arow[m] = W + static_cast<size_t>(clamp_row(row0 + m * 16 + li, V)) * D + 8 * kb;
+      if constexpr (PACKED)
+        arow[m] = packed_frag(W, min(row0 / 16 + static_cast<int>(m), V - 1), D, lane);
+      else
+        arow[m] = W + static_cast<size_t>(clamp_row(row0 + m * 16 + li, V)) * D + 8 * kb;
     });
     zero_acc(acc);
 
@@ -318,7 +341,7 @@ struct LdsLoop {
     stage_load(h, B, D, col0, 0, hreg);
     static_for<P>([&](auto p) FS_INLINE {
       const int q = min(static_cast<int>(p), nks - 1);
-      static_for<MR>([&](auto m) FS_INLINE { ring[p][m] = load_frag<NTL>(arow[m] + q * 32); });
+      static_for<MR>([&](auto m) FS_INLINE { ring[p][m] = load_frag<NTL>(arow[m] + q * kStep); });
     });
     stage_store(hs, hreg);
     __syncthreads();
@@ -335,7 +358,7 @@ struct LdsLoop {
             kstep(buf, s, ring[slot], acc);
             const int q = min(c * KS + s + P, nks - 1);
             static_for<MR>([&](auto m) FS_INLINE {
-              ring[slot][m] = load_frag<NTL>(arow[m] + q * 32);
+              ring[slot][m] = load_frag<NTL>(arow[m] + q * kStep);
             });
           });
         } else {
@@ -356,7 +379,7 @@ struct LdsLoop {
             if constexpr (n == NT - 1) {  // k step s done: refill its W slot
               const int q = min(c * KS + s + P, nks - 1);
               static_for<MR>([&](auto m) FS_INLINE {
-                ring[slot][m] = load_frag<NTL>(arow[m] + q * 32);
+                ring[slot][m] = load_frag<NTL>(arow[m] + q * kStep);
               });
             }
             __builtin_amdgcn_sched_barrier(0);
@@ -370,8 +393,11 @@ struct LdsLoop {
 };
 
 // ---------------------------------------------------------------------------
-// DmaLoop: every wave of the block owns MR*16 distinct vocabulary rows and
-// shares one batch tile of NT*16 rows.  h is staged into LDS by direct
+// DmaLoop: the block's waves form WR = NW/WB row groups x WB batch groups;
+// each wave computes MR*16 vocabulary rows against NT*16 batch rows (with
+// WB = 2 the two waves of a row group read the same W rows, the second
+// mostly from cache, and each reads only its half of the staged batch rows
+// from LDS: half the LDS bytes per MFMA).  h is staged into LDS by direct
 // global->LDS loads (no register round trip, no LDS store instructions) in a
 // ring of S KC-wide chunks issued S-1 chunks ahead; W fragments stream into a
 // ring of P k-steps held in registers.  Loads complete in issue order, so each
@@ -379,14 +405,17 @@ struct LdsLoop {
 // the W stream keeps its P-step lead across chunk boundaries.
 // Requires D % (KC * U) == 0.
 // ---------------------------------------------------------------------------
-template <int MR_, int NT_, int NW_, int KC, int P, int S, int BR, int G = 1, bool ROT = false>
+template <int MR_, int NT_, int NW_, int KC, int P, int S, int BR, int G = 1, bool ROT = false,
+          int WB_ = 1>
 struct DmaLoop {
   static constexpr int MR = MR_, NT = NT_, NW = NW_;
+  static constexpr int WB = WB_, WR = NW / WB;
+  static_assert(NW % WB == 0, "waves must tile the block");
   // the epilogue's per-row temperatures are loaded after the main loop
   // (loaded before it they would hold registers the loop needs)
   static constexpr bool kEarlyTemperature = false;
-  static constexpr int kRowsPerBlock = MR * 16 * NW;
-  static constexpr int kBlockCols = NT * 16;
+  static constexpr int kRowsPerBlock = MR * 16 * WR;
+  static constexpr int kBlockCols = NT * 16 * WB;
   static constexpr int KS = KC / 32;                 // MFMA k-steps per chunk
   static constexpr int CPR = KC / 8;                 // 16-byte pieces per staged row
   static constexpr int STAGE = kBlockCols * KC;      // bf16 elements per ring slot
@@ -418,8 +447,10 @@ struct DmaLoop {
   static constexpr size_t kMaxHBytes = 0x7FFFFFFF;  // buffer offsets are 32-bit
   // raw buffer resource word 3 for gfx9-family parts (untyped 32-bit data)
   static constexpr int kBufferFlags = 0x00020000;
-  __device__ __forceinline__ static int row0(int block, int wave) { return (block * NW + wave) * MR * 16; }
-  __device__ __forceinline__ static int col_off(int /*wave*/) { return 0; }
+  __device__ __forceinline__ static int row0(int block, int wave) {
+    return (block * WR + wave / WB) * MR * 16;
+  }
+  __device__ __forceinline__ static int col_off(int wave) { return (wave % WB) * NT * 16; }
   __device__ __forceinline__ static bool owns(int /*wave*/, int /*m*/, int /*n*/) { return true; }
 
   // Piece j of staged row n lives at slot j ^ (n mod CPR).
@@ -474,10 +505,15 @@ struct DmaLoop {
   __device__ __forceinline__ static bf16x8 bfrag(const __bf16* buf, int s, int n) {
     const int lane = threadIdx.x & (kWave - 1);
     const int li = lane & 15, kb = lane >> 4;
+    const int c0 = col_off(threadIdx.x >> 6);
     return __builtin_bit_cast(
-        bf16x8, *reinterpret_cast<const u32x4*>(buf + smem_off(n * 16 + li, s * 4 + kb)));
+        bf16x8, *reinterpret_cast<const u32x4*>(buf + smem_off(c0 + n * 16 + li, s * 4 + kb)));
   }
 
+  // PACKED: W is in fragment order (packed_frag), row0 is the wave's first
+  // grid row (a multiple of 16, not shifted) and V the number of groups.
+  static constexpr bool kPackedW = true;
+  template <bool PACKED = false>
   __device__ __forceinline__ static void run(const __bf16* __restrict__ W,
                                              const __bf16* __restrict__ h, int32_t B, int32_t D,
                                              int32_t V, int32_t row0, int32_t col0,
@@ -485,9 +521,13 @@ struct DmaLoop {
     const int lane = threadIdx.x & (kWave - 1);
     const int li = lane & 15, kb = lane >> 4;
     __bf16* hs = static_cast<__bf16*>(smem);
+    constexpr int kStep = PACKED ? kPackedStep : 32;  // elements between k-steps
     const __bf16* arow[MR];
     static_for<MR>([&](auto m) FS_INLINE {
-      arow[m] = W + static_cast<size_t>(clamp_row(row0 + m * 16 + li, V)) * D + 8 * kb;
+      if constexpr (PACKED)
+        arow[m] = packed_frag(W, min(row0 / 16 + static_cast<int>(m), V - 1), D, lane);
+      else
+        arow[m] = W + static_cast<size_t>(clamp_row(row0 + m * 16 + li, V)) * D + 8 * kb;
     });
     zero_acc(acc);
 
@@ -509,7 +549,7 @@ struct DmaLoop {
     bf16x8 ring[P][MR];
     static_for<P>([&](auto p) FS_INLINE {
       const int q = rq(min(static_cast<int>(p), nks - 1));
-      static_for<MR>([&](auto m) FS_INLINE { ring[p][m] = load_frag(arow[m] + q * 32); });
+      static_for<MR>([&](auto m) FS_INLINE { ring[p][m] = load_frag(arow[m] + q * kStep); });
     });
     __builtin_amdgcn_sched_barrier(0);
     // Chunk 0 staged.  The count leaves only chunks 1 .. S-2 in flight and
@@ -549,7 +589,7 @@ struct DmaLoop {
             static_for<G>([&](auto j) FS_INLINE {
               constexpr int sl = (g + 1 - G + decltype(j)::value) % P;
               const int q = rq(min(c * KS + s + 1 - G + decltype(j)::value + P, nks - 1));
-              static_for<MR>([&](auto m) FS_INLINE { ring[sl][m] = load_frag(arow[m] + q * 32); });
+              static_for<MR>([&](auto m) FS_INLINE { ring[sl][m] = load_frag(arow[m] + q * kStep); });
             });
           }
           __builtin_amdgcn_sched_barrier(0);

@@ -38,6 +38,12 @@ template <class L>
 struct XcdPaired : L {
   static constexpr bool kXcdPaired = true;
 };
+// Main loops that can read W in fragment order (packed_frag) declare kPackedW.
+template <class L, class = void>
+struct reads_packed_w : std::false_type {};
+template <class L>
+struct reads_packed_w<L, std::void_t<decltype(L::kPackedW)>> : std::bool_constant<L::kPackedW> {};
+
 template <class L, class = void>
 struct is_xcd_paired : std::false_type {};
 template <class L>
@@ -67,7 +73,7 @@ __device__ __forceinline__ void block_tile(const SampleArgs& a, int& tile, int& 
   }
 }
 
-template <class Loop, bool LSE>
+template <class Loop, bool LSE, bool PACKED = false>
 __global__ __launch_bounds__(Loop::NW * kWave)
 __attribute__((amdgpu_waves_per_eu(Loop::kWavesPerSimd))) void fused_sample_kernel(SampleArgs a) {
   constexpr int MR = Loop::MR, NT = Loop::NT, NW = Loop::NW;
@@ -99,7 +105,11 @@ __attribute__((amdgpu_waves_per_eu(Loop::kWavesPerSimd))) void fused_sample_kern
   if constexpr (Loop::kEarlyTemperature) load_temperatures();
 
   f32x4 acc[MR][NT];
-  Loop::run(a.W, a.h, a.B, a.D, a.V, row0, block_col0, acc, dyn_smem);
+  if constexpr (PACKED)  // fragment-order W: groups of the unshifted grid
+    Loop::template run<true>(a.W, a.h, a.B, a.D, (a.V + shift + 15) / 16, row0 + shift,
+                             block_col0, acc, dyn_smem);
+  else
+    Loop::run(a.W, a.h, a.B, a.D, a.V, row0, block_col0, acc, dyn_smem);
   if constexpr (!Loop::kEarlyTemperature) load_temperatures();
 
   // ---- epilogue: scale, perturb, running (max, argmax) per batch row ----
@@ -201,7 +211,7 @@ __attribute__((amdgpu_waves_per_eu(Loop::kWavesPerSimd))) void fused_sample_kern
 // persists across groups, so a block emits one partial per batch row.
 // Requires D == 32 * NW * KS.
 // ---------------------------------------------------------------------------
-template <int NT, int NW, int KS, int P, bool LSE>
+template <int NT, int NW, int KS, int P, bool LSE, bool PACKED = false>
 __global__ __launch_bounds__(NW * kWave) void persist_sample_kernel(SampleArgs a) {
   static_assert(KS % P == 0, "the load ring must tile a group");
   extern __shared__ __attribute__((aligned(16))) unsigned char dyn_smem[];
@@ -230,8 +240,14 @@ __global__ __launch_bounds__(NW * kWave) void persist_sample_kernel(SampleArgs a
     inv_t[n] = row_inv_temperature(T);
   });
 
+  // PACKED: W in fragment order (packed_frag); group g is packed group g
+  constexpr int kStep = PACKED ? kPackedStep : 32;  // elements between k-steps
   auto group_ptr = [&](int g) FS_INLINE {
-    return a.W + static_cast<size_t>(clamp_row(min(g, ngroups - 1) * 16 + li - shift, a.V)) * D + kbeg;
+    if constexpr (PACKED)
+      return packed_frag(a.W, min(g, ngroups - 1), D, lane) + wave * KS * kPackedStep;
+    else
+      return a.W + static_cast<size_t>(clamp_row(min(g, ngroups - 1) * 16 + li - shift, a.V)) * D +
+             kbeg;
   };
   const Philox philox(a.seed);
   ArgMax best[NT];
@@ -245,7 +261,7 @@ __global__ __launch_bounds__(NW * kWave) void persist_sample_kernel(SampleArgs a
   const __bf16* ap = group_ptr(g);
   const __bf16* ap_next = group_ptr(g + G);
   bf16x8 ring[P];
-  static_for<P>([&](auto p) FS_INLINE { ring[p] = load_frag(ap + p * 32); });
+  static_for<P>([&](auto p) FS_INLINE { ring[p] = load_frag(ap + p * kStep); });
 
   for (int it = 0; g < ngroups; g += G, ++it) {
     f32x4 acc[NT];
@@ -256,9 +272,9 @@ __global__ __launch_bounds__(NW * kWave) void persist_sample_kernel(SampleArgs a
       static_for<NT>([&](auto n) FS_INLINE { acc[n] = mfma16(ring[slot], hreg[s][n], acc[n]); });
       // refill with the k-step P ahead (the next group's, past the end of this one)
       if constexpr (s + P < KS)
-        ring[slot] = load_frag(ap + (s + P) * 32);
+        ring[slot] = load_frag(ap + (s + P) * kStep);
       else
-        ring[slot] = load_frag(ap_next + (s + P - KS) * 32);
+        ring[slot] = load_frag(ap_next + (s + P - KS) * kStep);
     });
     ap = ap_next;
     ap_next = group_ptr(g + 2 * G);
@@ -356,6 +372,19 @@ hipError_t launch_cfg(SampleArgs& a, hipStream_t stream) {
   const dim3 grid = is_xcd_paired<Loop>::value ? dim3((a.S + kXcds - 1) / kXcds * kXcds * nb)
                                                : dim3(a.S, nb);
   const dim3 block(Loop::NW * kWave);
+  if (a.w_packed) {
+    if constexpr (reads_packed_w<Loop>::value) {
+      if (a.part_lse != nullptr) return hipErrorInvalidValue;
+      if (smem > 0) {
+        static const hipError_t attr = allow_smem(&fused_sample_kernel<Loop, false, true>, smem);
+        if (attr != hipSuccess) return attr;
+      }
+      fused_sample_kernel<Loop, false, true><<<grid, block, smem, stream>>>(a);
+      return hipGetLastError();
+    } else {
+      return hipErrorInvalidValue;
+    }
+  }
   if (a.part_lse == nullptr)
     fused_sample_kernel<Loop, false><<<grid, block, smem, stream>>>(a);
   else
@@ -391,9 +420,9 @@ template <int NT, int NW, int KS, int P>
 struct Persist {
   static constexpr size_t kSmemBytes = 2ull * NW * NT * kWave * sizeof(f32x4);
   static bool supports(int32_t B, int32_t D) { return B <= NT * 16 && D == 32 * NW * KS; }
-  template <bool LSE>
+  template <bool LSE, bool PACKED = false>
   static hipError_t go(SampleArgs& a, hipStream_t stream) {
-    const auto kernel = persist_sample_kernel<NT, NW, KS, P, LSE>;
+    const auto kernel = persist_sample_kernel<NT, NW, KS, P, LSE, PACKED>;
     const int slots = resident_blocks(kernel, NW * kWave, kSmemBytes);
     if (slots <= 0) return hipErrorInvalidDevice;
     const int ngroups = (a.V + (a.vocab_offset & 3) + 15) / 16;
@@ -403,18 +432,20 @@ struct Persist {
   }
   static hipError_t launch(SampleArgs& a, hipStream_t stream) {
     if (!supports(a.B, a.D)) return hipErrorInvalidValue;
+    if (a.w_packed) return a.part_lse == nullptr ? go<false, true>(a, stream) : hipErrorInvalidValue;
     return a.part_lse == nullptr ? go<false>(a, stream) : go<true>(a, stream);
   }
 };
 
 template <class Loop>
 constexpr FusedConfig make_cfg(const char* name, int order) {
-  return {name, Loop::kRowsPerBlock, &launch_cfg<Loop>, &supports_cfg<Loop>, order};
+  return {name, Loop::kRowsPerBlock, &launch_cfg<Loop>, &supports_cfg<Loop>, order,
+          reads_packed_w<Loop>::value};
 }
 
 template <class Pol>
 constexpr FusedConfig make_persist(const char* name, int order) {
-  return {name, 16, &Pol::launch, &Pol::supports, order};
+  return {name, 16, &Pol::launch, &Pol::supports, order, true};
 }
 
 #define FS_STREAM(MR, NT, NW, P, NTL) \
@@ -439,6 +470,9 @@ constexpr FusedConfig make_persist(const char* name, int order) {
 #define FS_DMAP(MR, NT, NW, KC, P, S, BR, G)                                                  \
   make_cfg<XcdPaired<DmaLoop<MR, NT, NW, KC, P, S, BR, G>>>(                                 \
       "dmapair_mr" #MR "_nt" #NT "_nw" #NW "_kc" #KC "_p" #P "_s" #S "_br" #BR "_g" #G, 0)
+#define FS_DMAW(MR, NT, NW, KC, P, S, BR, G, WB)                                              \
+  make_cfg<DmaLoop<MR, NT, NW, KC, P, S, BR, G, false, WB>>(                                  \
+      "dma_mr" #MR "_nt" #NT "_nw" #NW "_kc" #KC "_p" #P "_s" #S "_br" #BR "_g" #G "_wb" #WB, 0)
 #define FS_PERSIST(NT, NW, KS, P) \
   make_persist<Persist<NT, NW, KS, P>>("persist_nt" #NT "_nw" #NW "_ks" #KS "_p" #P, 100 + NW)
 

@@ -224,3 +224,23 @@ def test_online_bounds_argument_errors(L):
     assert call(D=12) == bd.FS_ERR_INVALID_ARG
     assert call(ws=WS_ALIGNED + 8) == bd.FS_ERR_INVALID_ARG
     assert call(wsb=8) == bd.FS_ERR_WORKSPACE
+
+
+# ---- fragment-order weights ----
+def test_packed_sizes_and_errors(L):
+    assert L.fs_packed_weights_bytes(1000, 256, 0) == 63 * 16 * 256 * 2   # 1000 rows -> 63 groups
+    assert L.fs_packed_weights_bytes(1000, 256, 7) == 63 * 16 * 256 * 2   # shift 3: 1003 rows
+    assert L.fs_packed_weights_bytes(1024, 256, 1) == 65 * 16 * 256 * 2
+    assert L.fs_packed_weights_bytes(1000, 264, 0) == 0                   # D % 32 != 0
+    assert L.fs_packed_weights_bytes(0, 256, 0) == 0
+    need = L.fs_packed_weights_bytes(1000, 256, 0)
+    assert L.fs_pack_weights(ALIGNED, 1000, 264, 0, ALIGNED, 1 << 30, None) == bd.FS_ERR_INVALID_ARG
+    assert L.fs_pack_weights(None, 1000, 256, 0, ALIGNED, 1 << 30, None) == bd.FS_ERR_INVALID_ARG
+    assert L.fs_pack_weights(ALIGNED, 1000, 256, 0, ALIGNED + 8, 1 << 30, None) == bd.FS_ERR_INVALID_ARG
+    assert L.fs_pack_weights(ALIGNED, 1000, 256, 0, ALIGNED, need - 1, None) == bd.FS_ERR_WORKSPACE
+    # the packed sampler validates like fs_sample, plus D % 32
+    assert _sample(L, "fs_sample_packed", D=264) == bd.FS_ERR_INVALID_ARG
+    assert _sample(L, "fs_sample_packed", h=None) == bd.FS_ERR_INVALID_ARG
+    assert _sample(L, "fs_sample_packed", wsb=16) == bd.FS_ERR_WORKSPACE
+    assert _sample(L, "fs_sample_packed", B=0, h=None, W=None, T=None, ids=None, val=None,
+                   ws=None) == bd.FS_OK
