@@ -18,6 +18,9 @@ int fused_configs_small(const FusedConfig** out) {
       FS_KSPLIT(2, 1, 4, 8, 0),
       FS_KSPLIT(4, 2, 4, 4, 0),
       FS_STREAM(1, 1, 4, 8, 0),
+      FS_PERSISTN(1, 8, 16, 8),
+      FS_PERSISTN(2, 8, 16, 8),
+      FS_PERSISTN(1, 8, 32, 8),
   };
   *out = k;
   return static_cast<int>(sizeof(k) / sizeof(k[0]));

@@ -3,6 +3,7 @@
 // partials) and the noise diagnostics.  The sampler kernels themselves are
 // in fs_sampler.hpp, instantiated by fs_configs_*.hip.
 #include <cstring>
+#include <string>
 #include <vector>
 
 #include "fs_device.hpp"
@@ -210,7 +211,32 @@ double one_per_cu_fill(int id, int32_t V) {
 }
 }  // namespace
 
+static int auto_config_shape(int32_t B, int32_t D, int32_t V, bool packed);
+
+// The configuration with the same loop and tile shape but non-temporal W
+// loads (name + "_ntl1"), if there is one, else `id`.  On fragment-order W
+// each wave streams contiguous memory that is read exactly once, and the
+// non-temporal hint then raises the rate (Llama-3 head: 172 -> 158 us at
+// B = 1, 182 -> 163 us at B = 64, 269 -> 252 us at B = 256); on row-major W
+// it lowers it, so only the packed choice takes these twins.
+static int non_temporal_twin(int id) {
+  static const std::vector<int> twin = [] {
+    std::vector<int> t(configs().size());
+    for (size_t i = 0; i < t.size(); ++i) {
+      const int j = config_id((std::string(configs()[i].name) + "_ntl1").c_str());
+      t[i] = j >= 0 && configs()[j].packed_w ? j : static_cast<int>(i);
+    }
+    return t;
+  }();
+  return id >= 0 && id < static_cast<int>(twin.size()) ? twin[id] : id;
+}
+
 int fused_auto_config(int32_t B, int32_t D, int32_t V, bool packed) {
+  const int id = auto_config_shape(B, D, V, packed);
+  return packed ? non_temporal_twin(id) : id;
+}
+
+static int auto_config_shape(int32_t B, int32_t D, int32_t V, bool packed) {
   static const int persist[] = {config_id("persist_nt1_nw8_ks16_p8"),
                                 config_id("persist_nt2_nw8_ks16_p8"),
                                 config_id("persist_nt1_nw8_ks32_p8")};
@@ -253,16 +279,19 @@ int fused_auto_config(int32_t B, int32_t D, int32_t V, bool packed) {
   // gets the same bits as the same rows inside a whole-vocabulary call.
   //
   // On fragment-order (packed) W the 640-row blocks come first up to 128
-  // batch rows whenever they fill the CUs (Llama-3 head: 182 against 217 us
-  // at B = 64, 193 against 222 us at B = 128): each wave then streams five
-  // contiguous 16-row groups.
+  // batch rows whenever they fill the CUs (Llama-3 head, non-temporal twins:
+  // 163 against 194 us at B = 64, 175 against 194 us at B = 128): each wave
+  // then streams five contiguous 16-row groups.  At 256 batch rows the
+  // 64-wide staged chunks win at every D there (431 against 437 us on the
+  // Qwen3 head, 502 against 510 us at D = 8192).
   struct Pick { int dma[2]; int dma_short; int lds; };
   const int dma256_first = D <= 4096 ? dma256 : dma256_kc128;
   const Pick p = B <= 64    ? (packed ? Pick{{dma64_tall, dma64}, dma64_short, lds64}
                                       : Pick{{dma64, dma64_tall}, dma64_short, lds64})
                  : B <= 128 ? (packed ? Pick{{dma128_tall, dma128}, dma128_short, lds128}
                                       : Pick{{dma128, dma128_tall}, dma128_short, lds128})
-                 : B <= 256 ? Pick{{dma256_first, dma256}, dma256_short, lds256}
+                 : B <= 256 ? (packed ? Pick{{dma256, dma256_kc128}, dma256_short, lds256}
+                                      : Pick{{dma256_first, dma256}, dma256_short, lds256})
                             : Pick{{dma_paired, dma256_first}, dma256_short, lds256};
   // below three quarters of the CUs busy on average over the rounds the LDS
   // loop's smaller blocks win (sweeps: 0.58 loses by 15-30%, 0.77 wins by 2-5%)

@@ -406,7 +406,7 @@ struct LdsLoop {
 // Requires D % (KC * U) == 0.
 // ---------------------------------------------------------------------------
 template <int MR_, int NT_, int NW_, int KC, int P, int S, int BR, int G = 1, bool ROT = false,
-          int WB_ = 1>
+          int WB_ = 1, bool NTL = false>
 struct DmaLoop {
   static constexpr int MR = MR_, NT = NT_, NW = NW_;
   static constexpr int WB = WB_, WR = NW / WB;
@@ -549,7 +549,7 @@ struct DmaLoop {
     bf16x8 ring[P][MR];
     static_for<P>([&](auto p) FS_INLINE {
       const int q = rq(min(static_cast<int>(p), nks - 1));
-      static_for<MR>([&](auto m) FS_INLINE { ring[p][m] = load_frag(arow[m] + q * kStep); });
+      static_for<MR>([&](auto m) FS_INLINE { ring[p][m] = load_frag<NTL>(arow[m] + q * kStep); });
     });
     __builtin_amdgcn_sched_barrier(0);
     // Chunk 0 staged.  The count leaves only chunks 1 .. S-2 in flight and
@@ -589,7 +589,7 @@ struct DmaLoop {
             static_for<G>([&](auto j) FS_INLINE {
               constexpr int sl = (g + 1 - G + decltype(j)::value) % P;
               const int q = rq(min(c * KS + s + 1 - G + decltype(j)::value + P, nks - 1));
-              static_for<MR>([&](auto m) FS_INLINE { ring[sl][m] = load_frag(arow[m] + q * kStep); });
+              static_for<MR>([&](auto m) FS_INLINE { ring[sl][m] = load_frag<NTL>(arow[m] + q * kStep); });
             });
           }
           __builtin_amdgcn_sched_barrier(0);

@@ -211,7 +211,7 @@ __attribute__((amdgpu_waves_per_eu(Loop::kWavesPerSimd))) void fused_sample_kern
 // persists across groups, so a block emits one partial per batch row.
 // Requires D == 32 * NW * KS.
 // ---------------------------------------------------------------------------
-template <int NT, int NW, int KS, int P, bool LSE, bool PACKED = false>
+template <int NT, int NW, int KS, int P, bool LSE, bool PACKED = false, bool NTL = false>
 __global__ __launch_bounds__(NW * kWave) void persist_sample_kernel(SampleArgs a) {
   static_assert(KS % P == 0, "the load ring must tile a group");
   extern __shared__ __attribute__((aligned(16))) unsigned char dyn_smem[];
@@ -261,7 +261,7 @@ __global__ __launch_bounds__(NW * kWave) void persist_sample_kernel(SampleArgs a
   const __bf16* ap = group_ptr(g);
   const __bf16* ap_next = group_ptr(g + G);
   bf16x8 ring[P];
-  static_for<P>([&](auto p) FS_INLINE { ring[p] = load_frag(ap + p * kStep); });
+  static_for<P>([&](auto p) FS_INLINE { ring[p] = load_frag<NTL>(ap + p * kStep); });
 
   for (int it = 0; g < ngroups; g += G, ++it) {
     f32x4 acc[NT];
@@ -272,9 +272,9 @@ __global__ __launch_bounds__(NW * kWave) void persist_sample_kernel(SampleArgs a
       static_for<NT>([&](auto n) FS_INLINE { acc[n] = mfma16(ring[slot], hreg[s][n], acc[n]); });
       // refill with the k-step P ahead (the next group's, past the end of this one)
       if constexpr (s + P < KS)
-        ring[slot] = load_frag(ap + (s + P) * kStep);
+        ring[slot] = load_frag<NTL>(ap + (s + P) * kStep);
       else
-        ring[slot] = load_frag(ap_next + (s + P - KS) * kStep);
+        ring[slot] = load_frag<NTL>(ap_next + (s + P - KS) * kStep);
     });
     ap = ap_next;
     ap_next = group_ptr(g + 2 * G);
@@ -416,13 +416,13 @@ int resident_blocks(Kernel kernel, int threads, size_t smem) {
   return cached;
 }
 
-template <int NT, int NW, int KS, int P>
+template <int NT, int NW, int KS, int P, bool NTL = false>
 struct Persist {
   static constexpr size_t kSmemBytes = 2ull * NW * NT * kWave * sizeof(f32x4);
   static bool supports(int32_t B, int32_t D) { return B <= NT * 16 && D == 32 * NW * KS; }
   template <bool LSE, bool PACKED = false>
   static hipError_t go(SampleArgs& a, hipStream_t stream) {
-    const auto kernel = persist_sample_kernel<NT, NW, KS, P, LSE, PACKED>;
+    const auto kernel = persist_sample_kernel<NT, NW, KS, P, LSE, PACKED, NTL>;
     const int slots = resident_blocks(kernel, NW * kWave, kSmemBytes);
     if (slots <= 0) return hipErrorInvalidDevice;
     const int ngroups = (a.V + (a.vocab_offset & 3) + 15) / 16;
@@ -473,6 +473,14 @@ constexpr FusedConfig make_persist(const char* name, int order) {
 #define FS_DMAW(MR, NT, NW, KC, P, S, BR, G, WB)                                              \
   make_cfg<DmaLoop<MR, NT, NW, KC, P, S, BR, G, false, WB>>(                                  \
       "dma_mr" #MR "_nt" #NT "_nw" #NW "_kc" #KC "_p" #P "_s" #S "_br" #BR "_g" #G "_wb" #WB, 0)
+#define FS_PERSISTN(NT, NW, KS, P) \
+  make_persist<Persist<NT, NW, KS, P, true>>("persist_nt" #NT "_nw" #NW "_ks" #KS "_p" #P "_ntl1", 100 + NW)
+#define FS_DMAN(MR, NT, NW, KC, P, S, BR, G)                                                  \
+  make_cfg<DmaLoop<MR, NT, NW, KC, P, S, BR, G, false, 1, true>>(                            \
+      "dma_mr" #MR "_nt" #NT "_nw" #NW "_kc" #KC "_p" #P "_s" #S "_br" #BR "_g" #G "_ntl1", 0)
+#define FS_DMAPN(MR, NT, NW, KC, P, S, BR, G)                                                 \
+  make_cfg<XcdPaired<DmaLoop<MR, NT, NW, KC, P, S, BR, G, false, 1, true>>>(                  \
+      "dmapair_mr" #MR "_nt" #NT "_nw" #NW "_kc" #KC "_p" #P "_s" #S "_br" #BR "_g" #G "_ntl1", 0)
 #define FS_PERSIST(NT, NW, KS, P) \
   make_persist<Persist<NT, NW, KS, P>>("persist_nt" #NT "_nw" #NW "_ks" #KS "_p" #P, 100 + NW)
 
