@@ -285,7 +285,7 @@ def main():
         del graph
         plain = next((e["us_per_step"] for e in sweep if e["B"] == b), None)
         grouped.append({"B": b, "groups": G, "us_per_step": round(gt, 2),
-                        "fs_sample_us_per_step": plain})
+                        "whole_vocabulary_us_per_step": plain})
         del h_g, T_g, pv, pi, pl, ws, outs
 
     # Online sampler with early finalisation: fs_sample_online per step over
@@ -308,6 +308,9 @@ def main():
             for kind in ("confident", "random"):
                 W_o = (wl.make_confident_w(wlk, h_o, chunk_rows=V // 8, later_std=0.002,
                                            device=dev) if kind == "confident" else W)
+                # chunks run on the fragment-order copy when there is one
+                W_run = (fsl.pack_weights(W_o) if kind == "confident" else Wp) if Wp is not None \
+                    else W_o
                 for cuts in splits:
                     n_chunks = len(cuts) - 1
                     bt = time_steps(torch, lambda i: fsl.online_bounds(W_o, cuts), 3, 1,
@@ -315,11 +318,11 @@ def main():
                     later = fsl.online_bounds(W_o, cuts)
                     ws = fsl.alloc_workspace(fsl.online_workspace_bytes(b, D, V, n_chunks), dev)
 
-                    def ofn(i, h_o=h_o, T_o=T_o, W_o=W_o, cuts=cuts, later=later, outs=outs,
+                    def ofn(i, h_o=h_o, T_o=T_o, W_run=W_run, cuts=cuts, later=later, outs=outs,
                             ws=ws):
                         seed, step = wlk.sampler_seed(i)
-                        fsl.sample_online(h_o, W_o, T_o, seed, step, cuts, later, out=outs,
-                                          workspace=ws)
+                        fsl.sample_online(h_o, W_run, T_o, seed, step, cuts, later, out=outs,
+                                          workspace=ws, V=V)
                     for i in range(3):
                         ofn(i)
                     torch.cuda.synchronize()
@@ -332,14 +335,16 @@ def main():
                     torch.cuda.synchronize()
                     used = outs[2].float().mean().item()
                     del graph
-                    plain = next((e["us_per_step"] for e in sweep if e["B"] == b), None)
+                    plain = next((e.get("packed_us_per_step" if Wp is not None else "us_per_step")
+                                  for e in sweep if e["B"] == b), None)
                     online.append({"B": b, "weights": kind, "chunks": n_chunks,
+                                   "w_layout": "fragment order" if Wp is not None else "row-major",
                                    "first_chunk_rows": cuts[1],
                                    "us_per_step": round(ot, 2),
                                    "mean_chunks_used": round(used, 3),
-                                   "fs_sample_us_per_step": plain, "bounds_us": round(bt, 1)})
+                                   "whole_vocabulary_us_per_step": plain, "bounds_us": round(bt, 1)})
                     del later, ws
-                del W_o
+                del W_o, W_run
             del h_o, T_o, outs
             torch.cuda.empty_cache()
 

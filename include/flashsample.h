@@ -229,6 +229,18 @@ FS_API fs_status fs_sample_online(const void* h, const void* W, int32_t B, int32
                                   int32_t n_chunks, const double* later_norm, int32_t* out_ids,
                                   float* out_maxval, int32_t* out_chunks, void* workspace,
                                   size_t workspace_bytes, void* stream);
+/* The same on fragment-order weights (fs_pack_weights at the same
+ * vocab_offset mod 4): W_packed in place of W, every chunk start cuts[c]
+ * (0 < c < n_chunks) a multiple of 16, D % 32 == 0 (FS_ERR_INVALID_ARG
+ * otherwise).  later_norm comes from fs_online_bounds on the row-major W.
+ * Results as fs_sample_packed over the whole W. */
+FS_API fs_status fs_sample_online_packed(const void* h, const void* W_packed, int32_t B,
+                                         int32_t D, int32_t V, int32_t vocab_offset,
+                                         const float* temperature, uint64_t seed, uint64_t step,
+                                         const int32_t* cuts, int32_t n_chunks,
+                                         const double* later_norm, int32_t* out_ids,
+                                         float* out_maxval, int32_t* out_chunks,
+                                         void* workspace, size_t workspace_bytes, void* stream);
 
 /* The standard unfused decode step the method replaces (wiki summary,
  * "Method", first paragraph): (1) matmul writing fp32 logits [B][V] to

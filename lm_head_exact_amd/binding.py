@@ -69,6 +69,8 @@ def lib():
         ("fs_online_bounds", [vp, i32, i32, vp, i32, vp, vp, sz, vp], ctypes.c_int),
         ("fs_sample_online", [vp, vp, i32, i32, i32, i32, vp, u64, u64, vp, i32, vp, vp, vp,
                               vp, vp, sz, vp], ctypes.c_int),
+        ("fs_sample_online_packed", [vp, vp, i32, i32, i32, i32, vp, u64, u64, vp, i32, vp, vp,
+                                     vp, vp, vp, sz, vp], ctypes.c_int),
         ("fs_debug_noise", [u64, u64, u32, u32, i64, vp, vp, vp], ctypes.c_int),
         ("fs_debug_gumbel", [vp, i64, vp, vp], ctypes.c_int),
         ("fs_num_configs", [], i32),
@@ -340,17 +342,27 @@ def online_workspace_bytes(B: int, D: int, V: int, n_chunks: int) -> int:
 
 
 def sample_online(h, W, temperature, seed, step, cuts, later_norm, vocab_offset=0, out=None,
-                  workspace=None):
+                  workspace=None, V=None):
     """Online sampler with early finalisation over the chunks W[cuts[c]:cuts[c+1]]:
-    returns (ids int32[B], maxval fp32[B], chunks int32[B])."""
+    returns (ids int32[B], maxval fp32[B], chunks int32[B]).  W is the row-major
+    V x D matrix, or (1-D, with V given) its fragment-order copy from
+    pack_weights, whose chunk starts must be multiples of 16."""
     _req(h, "h", torch.bfloat16, 2)
-    _req(W, "W", torch.bfloat16, 2)
+    packed = W.dim() == 1
+    _req(W, "W", torch.bfloat16, 1 if packed else 2)
     _req(temperature, "temperature", torch.float32, 1)
     _req(later_norm, "later_norm", torch.float64, 1)
     B, D = h.shape
-    V, D2 = W.shape
-    if D2 != D:
-        raise ValueError(f"h is B x {D} but W is V x {D2}")
+    if packed:
+        if V is None:
+            raise ValueError("V is required with fragment-order W")
+        need = packed_weights_bytes(V, D, vocab_offset)
+        if need == 0 or W.numel() * 2 < need:
+            raise ValueError(f"W_packed holds {W.numel() * 2} bytes; {need} needed")
+    else:
+        V, D2 = W.shape
+        if D2 != D:
+            raise ValueError(f"h is B x {D} but W is V x {D2}")
     if temperature.shape[0] != B:
         raise ValueError("temperature must have B entries")
     arr, n = _host_cuts(cuts)
@@ -366,7 +378,8 @@ def sample_online(h, W, temperature, seed, step, cuts, later_norm, vocab_offset=
         raise ValueError("all tensors must be on one device")
     if workspace is None:
         workspace = alloc_workspace(online_workspace_bytes(B, D, V, n), dev)
-    _check(lib().fs_sample_online(
+    fn = lib().fs_sample_online_packed if packed else lib().fs_sample_online
+    _check(fn(
         _ptr(h), _ptr(W), B, D, V, int(vocab_offset), _ptr(temperature),
         int(seed) & (2**64 - 1), int(step) & (2**64 - 1), arr, n, _ptr(later_norm), _ptr(ids),
         _ptr(val), _ptr(chunks), _ptr(workspace), workspace.numel() * workspace.element_size(),

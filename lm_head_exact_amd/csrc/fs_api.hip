@@ -205,6 +205,93 @@ size_t online_workspace(int32_t B, int32_t V, int32_t n_chunks) {
          fs::round_up(sizeof(int32_t) * B, 256) + fs::round_up(sizeof(int32_t) * n_chunks, 256);
 }
 
+// Shared body of fs_sample_online / fs_sample_online_packed (W in fragment
+// order: every chunk starts on a 16-row group of the packed layout).
+static fs_status run_online(const void* h, const void* W, int32_t B, int32_t D, int32_t V,
+                            int32_t vocab_offset, const float* temperature, uint64_t seed,
+                            uint64_t step, const int32_t* cuts, int32_t n_chunks,
+                            const double* later_norm, int32_t* out_ids, float* out_maxval,
+                            int32_t* out_chunks, void* workspace, size_t workspace_bytes,
+                            void* stream, bool packed, const char* who) {
+  fs_status s = check_sample_args(h, W, B, D, V, vocab_offset, temperature, out_ids, out_maxval,
+                                  workspace);
+  if (s != FS_OK) return s;
+  if ((s = check_cuts(cuts, n_chunks, V, who)) != FS_OK) return s;
+  if (B == 0) return FS_OK;
+  if (!out_chunks || !later_norm) return fail(FS_ERR_INVALID_ARG, "null pointer argument");
+  if (!aligned(out_chunks, 4) || !aligned(later_norm, 8))
+    return fail(FS_ERR_INVALID_ARG, "out_chunks must be 4-byte and later_norm 8-byte aligned");
+  if (packed) {
+    if (D % 32 != 0)
+      return fail(FS_ERR_INVALID_ARG, "%s: D must be a multiple of 32 (got %d)", who, D);
+    for (int32_t c = 1; c < n_chunks; ++c)
+      if (cuts[c] % 16 != 0)
+        return fail(FS_ERR_INVALID_ARG, "%s: chunk starts must be multiples of 16 (cuts[%d]=%d)",
+                    who, c, cuts[c]);
+  }
+  if (D > kMaxOnlineD)
+    return fail(FS_ERR_UNSUPPORTED, "%s: D=%d exceeds %d, where the bound's rounding margin holds",
+                who, D, kMaxOnlineD);
+  const size_t need = online_workspace(B, V, n_chunks);
+  if (workspace_bytes < need)
+    return fail(FS_ERR_WORKSPACE, "%s: workspace of %zu bytes is below the %zu required", who,
+                workspace_bytes, need);
+  // the chunks' configurations, checked before anything is launched
+  for (int32_t c = 0; c < n_chunks; ++c) {
+    const int cfg = choose_config(B, D, cuts[c + 1] - cuts[c], packed);
+    if (!fs::fused_config_supports(cfg, B, D))
+      return fail(FS_ERR_UNSUPPORTED, "%s: forced configuration %s does not support B=%d, D=%d",
+                  who, fs::fused_config_name(cfg), B, D);
+    if (packed && !fs::fused_config_reads_packed(cfg))
+      return fail(FS_ERR_UNSUPPORTED, "%s: configuration %s has no packed-W kernel", who,
+                  fs::fused_config_name(cfg));
+  }
+  const size_t S = max_splits(V);
+  const size_t region = fs::round_up(sizeof(float) * B * S, 256);
+  char* ws = static_cast<char*>(workspace);
+  float* part_val = reinterpret_cast<float*>(ws);
+  int32_t* part_idx = reinterpret_cast<int32_t*>(ws + region);
+  char* tail = ws + fused_workspace(B, V);
+  double* hnorm = reinterpret_cast<double*>(tail);
+  tail += fs::round_up(sizeof(double) * B, 256);
+  int32_t* done = reinterpret_cast<int32_t*>(tail);
+  tail += fs::round_up(sizeof(int32_t) * B, 256);
+  int32_t* live = reinterpret_cast<int32_t*>(tail);
+  // largest value of the Gumbel map on the uniform grid: u = 1 - 2^-24
+  const double g_max = -std::log(-std::log1p(-0x1p-24));
+  const double margin = 1.0 + 0x1p-8;
+  const hipStream_t st = static_cast<hipStream_t>(stream);
+  hipError_t e = fs::launch_online_init(static_cast<const __bf16*>(h), B, D, n_chunks, hnorm,
+                                        done, live, out_ids, out_maxval, out_chunks, st);
+  if (e != hipSuccess) return hip_fail(e, "online init launch");
+  for (int32_t c = 0; c < n_chunks; ++c) {
+    fs::SampleArgs a;
+    a.h = static_cast<const __bf16*>(h);
+    // a packed chunk starts at group cuts[c] / 16 of 16 rows x D
+    a.W = static_cast<const __bf16*>(W) + static_cast<size_t>(cuts[c]) * D;
+    a.B = B;
+    a.D = D;
+    a.V = cuts[c + 1] - cuts[c];
+    a.vocab_offset = vocab_offset + cuts[c];
+    a.temperature = temperature;
+    a.seed = seed;
+    a.step = step;
+    a.part_val = part_val;
+    a.part_idx = part_idx;
+    a.part_lse = nullptr;
+    a.S = 0;
+    a.live = c > 0 ? live + (c - 1) : nullptr;
+    a.w_packed = packed;
+    e = fs::launch_fused(choose_config(B, D, a.V, packed), a, st);
+    if (e != hipSuccess) return hip_fail(e, "fused sampler launch");
+    e = fs::launch_online_step(part_val, part_idx, a.S, B, c, n_chunks, later_norm, hnorm,
+                               temperature, g_max, margin, done, live, out_ids, out_maxval,
+                               out_chunks, st);
+    if (e != hipSuccess) return hip_fail(e, "online step launch");
+  }
+  return FS_OK;
+}
+
 }  // namespace
 
 extern "C" {
@@ -348,71 +435,20 @@ fs_status fs_sample_online(const void* h, const void* W, int32_t B, int32_t D, i
                            const double* later_norm, int32_t* out_ids, float* out_maxval,
                            int32_t* out_chunks, void* workspace, size_t workspace_bytes,
                            void* stream) {
-  const char* who = "fs_sample_online";
-  fs_status s = check_sample_args(h, W, B, D, V, vocab_offset, temperature, out_ids, out_maxval,
-                                  workspace);
-  if (s != FS_OK) return s;
-  if ((s = check_cuts(cuts, n_chunks, V, who)) != FS_OK) return s;
-  if (B == 0) return FS_OK;
-  if (!out_chunks || !later_norm) return fail(FS_ERR_INVALID_ARG, "null pointer argument");
-  if (!aligned(out_chunks, 4) || !aligned(later_norm, 8))
-    return fail(FS_ERR_INVALID_ARG, "out_chunks must be 4-byte and later_norm 8-byte aligned");
-  if (D > kMaxOnlineD)
-    return fail(FS_ERR_UNSUPPORTED, "%s: D=%d exceeds %d, where the bound's rounding margin holds",
-                who, D, kMaxOnlineD);
-  const size_t need = online_workspace(B, V, n_chunks);
-  if (workspace_bytes < need)
-    return fail(FS_ERR_WORKSPACE, "%s: workspace of %zu bytes is below the %zu required", who,
-                workspace_bytes, need);
-  // the chunks' configurations, checked before anything is launched
-  for (int32_t c = 0; c < n_chunks; ++c) {
-    const int cfg = choose_config(B, D, cuts[c + 1] - cuts[c]);
-    if (!fs::fused_config_supports(cfg, B, D))
-      return fail(FS_ERR_UNSUPPORTED, "%s: forced configuration %s does not support B=%d, D=%d",
-                  who, fs::fused_config_name(cfg), B, D);
-  }
-  const size_t S = max_splits(V);
-  const size_t region = fs::round_up(sizeof(float) * B * S, 256);
-  char* ws = static_cast<char*>(workspace);
-  float* part_val = reinterpret_cast<float*>(ws);
-  int32_t* part_idx = reinterpret_cast<int32_t*>(ws + region);
-  char* tail = ws + fused_workspace(B, V);
-  double* hnorm = reinterpret_cast<double*>(tail);
-  tail += fs::round_up(sizeof(double) * B, 256);
-  int32_t* done = reinterpret_cast<int32_t*>(tail);
-  tail += fs::round_up(sizeof(int32_t) * B, 256);
-  int32_t* live = reinterpret_cast<int32_t*>(tail);
-  // largest value of the Gumbel map on the uniform grid: u = 1 - 2^-24
-  const double g_max = -std::log(-std::log1p(-0x1p-24));
-  const double margin = 1.0 + 0x1p-8;
-  const hipStream_t st = static_cast<hipStream_t>(stream);
-  hipError_t e = fs::launch_online_init(static_cast<const __bf16*>(h), B, D, n_chunks, hnorm,
-                                        done, live, out_ids, out_maxval, out_chunks, st);
-  if (e != hipSuccess) return hip_fail(e, "online init launch");
-  for (int32_t c = 0; c < n_chunks; ++c) {
-    fs::SampleArgs a;
-    a.h = static_cast<const __bf16*>(h);
-    a.W = static_cast<const __bf16*>(W) + static_cast<size_t>(cuts[c]) * D;
-    a.B = B;
-    a.D = D;
-    a.V = cuts[c + 1] - cuts[c];
-    a.vocab_offset = vocab_offset + cuts[c];
-    a.temperature = temperature;
-    a.seed = seed;
-    a.step = step;
-    a.part_val = part_val;
-    a.part_idx = part_idx;
-    a.part_lse = nullptr;
-    a.S = 0;
-    a.live = c > 0 ? live + (c - 1) : nullptr;
-    e = fs::launch_fused(choose_config(B, D, a.V), a, st);
-    if (e != hipSuccess) return hip_fail(e, "fused sampler launch");
-    e = fs::launch_online_step(part_val, part_idx, a.S, B, c, n_chunks, later_norm, hnorm,
-                               temperature, g_max, margin, done, live, out_ids, out_maxval,
-                               out_chunks, st);
-    if (e != hipSuccess) return hip_fail(e, "online step launch");
-  }
-  return FS_OK;
+  return run_online(h, W, B, D, V, vocab_offset, temperature, seed, step, cuts, n_chunks,
+                    later_norm, out_ids, out_maxval, out_chunks, workspace, workspace_bytes,
+                    stream, false, "fs_sample_online");
+}
+
+fs_status fs_sample_online_packed(const void* h, const void* W_packed, int32_t B, int32_t D,
+                                  int32_t V, int32_t vocab_offset, const float* temperature,
+                                  uint64_t seed, uint64_t step, const int32_t* cuts,
+                                  int32_t n_chunks, const double* later_norm, int32_t* out_ids,
+                                  float* out_maxval, int32_t* out_chunks, void* workspace,
+                                  size_t workspace_bytes, void* stream) {
+  return run_online(h, W_packed, B, D, V, vocab_offset, temperature, seed, step, cuts, n_chunks,
+                    later_norm, out_ids, out_maxval, out_chunks, workspace, workspace_bytes,
+                    stream, true, "fs_sample_online_packed");
 }
 
 fs_status fs_merge(const float* partial_val, const int32_t* partial_idx, int32_t P, int32_t B,

@@ -244,3 +244,17 @@ def test_packed_sizes_and_errors(L):
     assert _sample(L, "fs_sample_packed", wsb=16) == bd.FS_ERR_WORKSPACE
     assert _sample(L, "fs_sample_packed", B=0, h=None, W=None, T=None, ids=None, val=None,
                    ws=None) == bd.FS_OK
+
+
+def test_online_packed_argument_errors(L):
+    def call(cuts, n=2, D=256, **kw):
+        a = dict(h=ALIGNED, W=ALIGNED, B=4, V=1000, off=0, T=ALIGNED, later=ALIGNED, ids=ALIGNED,
+                 val=ALIGNED, chunks=ALIGNED, ws=WS_ALIGNED, wsb=1 << 30)
+        a.update(kw)
+        return L.fs_sample_online_packed(a["h"], a["W"], a["B"], D, a["V"], a["off"], a["T"], 1, 2,
+                                         cuts, n, a["later"], a["ids"], a["val"], a["chunks"],
+                                         a["ws"], a["wsb"], None)
+    assert call(_cuts(0, 500, 1000)) == bd.FS_ERR_INVALID_ARG        # 500 % 16 != 0
+    assert call(_cuts(0, 512, 1000), D=264) == bd.FS_ERR_INVALID_ARG  # D % 32 != 0
+    assert call(_cuts(0, 512, 999)) == bd.FS_ERR_INVALID_ARG          # does not end at V
+    assert call(_cuts(0, 512, 1000), wsb=16) == bd.FS_ERR_WORKSPACE

@@ -257,3 +257,55 @@ def test_captured_graph_replays_match_eager():
         for a, b in zip(out, ref):
             assert torch.equal(a, b), f"replay {r}"
     assert (ref[2] == 1).any() and (ref[2] > 1).any()
+
+
+# ---- fragment-order (packed) weights ----
+def _run_packed(h, W, T, seed, step, cuts, off=0):
+    hd, Wd, Td = h.to(DEV), W.to(DEV), torch.as_tensor(T).to(DEV)
+    later = fsl.online_bounds(Wd, cuts)
+    Wp = fsl.pack_weights(Wd, off)
+    ids, val, used = fsl.sample_online(hd, Wp, Td, seed, step, cuts, later, vocab_offset=off,
+                                       V=W.shape[0])
+    torch.cuda.synchronize()
+    return to_host(ids), to_host(val), to_host(used)
+
+
+@pytest.mark.parametrize("norm", [8.0, 60.0])
+@pytest.mark.parametrize("B,off", [(5, 0), (40, 3), (300, 6)])
+def test_packed_aligned_rows_stop_early(norm, B, off):
+    D, V, c0 = 128, 2400, 320
+    h, W = _aligned(B, D, V, c0, seed=B + 1, norm=norm)
+    T = np.resize(np.asarray(TEMPS, np.float32), B)
+    cuts = np.array([0, c0, 896, 1296, V])
+    ids, val, used = _run_packed(h, W, T, 31, 7, cuts, off)
+    o_used = _check(wl.bf16_bits(h), wl.bf16_bits(W), T, 31, 7, cuts, off, ids, val, used,
+                    label=f"packed aligned norm={norm} B={B}")
+    if norm == 60.0:
+        assert np.all(o_used == 1)
+
+
+@pytest.mark.parametrize("B", [32, 256])
+def test_packed_full_size_confident_and_random(B):
+    """Llama-3-8B-shaped head in 8 chunks of 16032 rows (multiples of 16) on
+    fragment-order W: confident weights stop after the first chunk, random
+    weights use all 8; sampled rows against the oracle."""
+    w = wl.LLAMA3_8B
+    h = wl.make_h(w, B, DEV)
+    T = wl.make_temperature(w, B, DEV)
+    cuts = np.arange(0, w.V + 1, w.V // 8)
+    rows = sample_rows(B, k=4, seed=B + 1)
+    hb, Tb = wl.bf16_bits(h), to_host(T)
+    for kind in ("confident", "random"):
+        W = (wl.make_confident_w(w, h, chunk_rows=w.V // 8, later_std=0.002, device=DEV)
+             if kind == "confident" else wl.make_w(w, DEV))
+        seed, step = w.sampler_seed(4)
+        later = fsl.online_bounds(W, cuts)
+        Wp = fsl.pack_weights(W)
+        ids, val, used = fsl.sample_online(h, Wp, T, seed, step, cuts, later, V=w.V)
+        torch.cuda.synchronize()
+        del Wp
+        ids, val, used = to_host(ids), to_host(val), to_host(used)
+        Wb = wl.bf16_bits(W)
+        del W
+        assert np.all(used == (1 if kind == "confident" else 8)), used
+        check_rows(hb, Wb, Tb, seed, step, 0, ids, val, rows=rows, label=f"packed {kind} B={B}")
