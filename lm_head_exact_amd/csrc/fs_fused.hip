@@ -251,6 +251,7 @@ static int auto_config_shape(int32_t B, int32_t D, int32_t V, bool packed) {
   static const int dma256 = config_id("dma_mr2_nt16_nw8_kc64_p4_s4_br4_g2");
   static const int dma256_kc128 = config_id("dma_mr2_nt16_nw8_kc128_p4_s2_br4_g2");
   static const int dma_paired = config_id("dmapair_mr2_nt16_nw8_kc128_p4_s2_br4_g2");
+  static const int dma_paired_kc64 = config_id("dmapair_mr2_nt16_nw8_kc64_p4_s4_br4_g2");
   static const int dma64_short = config_id("dma_mr1_nt4_nw4_kc64_p8_s3_br4_g2");
   static const int dma128_short = config_id("dma_mr1_nt8_nw4_kc64_p8_s3_br4_g2");
   static const int dma256_short = config_id("dma_mr1_nt16_nw4_kc64_p8_s3_br4_g2");
@@ -283,7 +284,9 @@ static int auto_config_shape(int32_t B, int32_t D, int32_t V, bool packed) {
   // 163 against 194 us at B = 64, 175 against 194 us at B = 128): each wave
   // then streams five contiguous 16-row groups.  At 256 batch rows the
   // 64-wide staged chunks win at every D there (431 against 437 us on the
-  // Qwen3 head, 502 against 510 us at D = 8192).
+  // Qwen3 head, 502 against 510 us at D = 8192), and on the paired grid above
+  // 256 batch rows (B = 512: 873 against 917 us at D = 8192, 483 against 500
+  // us on the Llama-3 head, 681 against 708 us on the Qwen3 head).
   struct Pick { int dma[2]; int dma_short; int lds; };
   const int dma256_first = D <= 4096 ? dma256 : dma256_kc128;
   const Pick p = B <= 64    ? (packed ? Pick{{dma64_tall, dma64}, dma64_short, lds64}
@@ -292,6 +295,7 @@ static int auto_config_shape(int32_t B, int32_t D, int32_t V, bool packed) {
                                       : Pick{{dma128, dma128_tall}, dma128_short, lds128})
                  : B <= 256 ? (packed ? Pick{{dma256, dma256_kc128}, dma256_short, lds256}
                                       : Pick{{dma256_first, dma256}, dma256_short, lds256})
+                 : packed   ? Pick{{dma_paired_kc64, dma256}, dma256_short, lds256}
                             : Pick{{dma_paired, dma256_first}, dma256_short, lds256};
   // below three quarters of the CUs busy on average over the rounds the LDS
   // loop's smaller blocks win (sweeps: 0.58 loses by 15-30%, 0.77 wins by 2-5%)
