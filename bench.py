@@ -84,7 +84,7 @@ def kernel_sources_sha256():
     h = hashlib.sha256()
     for name in ("fs_device.hpp", "fs_internal.hpp", "fs_mma.hpp", "fs_sampler.hpp",
                  "fs_configs_small.hip", "fs_configs_lds.hip",
-                 "fs_configs_dma_a.hip", "fs_configs_dma_b.hip"):
+                 "fs_configs_dma_a.hip", "fs_configs_dma_b.hip", "fs_configs_dma_ntl.hip"):
         h.update(name.encode())
         h.update(open(os.path.join(csrc, name), "rb").read())
     return h.hexdigest()
@@ -269,8 +269,12 @@ def main():
         def gfn(i, h_g=h_g, T_g=T_g, pv=pv, pi=pi, pl=pl, ws=ws, outs=outs, G=G, Vg=Vg):
             seed, step = wlk.sampler_seed(i)
             for p in range(G):
-                fsl.sample_partial_lse(h_g, W[p * Vg:(p + 1) * Vg], T_g, seed, step, p * Vg,
-                                       pv[p], pi[p], pl[p], workspace=ws)
+                if Wp is not None:  # group p of the fragment-order W (Vg % 16 == 0)
+                    fsl.sample_partial_lse(h_g, Wp[p * Vg * D:(p + 1) * Vg * D], T_g, seed, step,
+                                           p * Vg, pv[p], pi[p], pl[p], workspace=ws, V=Vg)
+                else:
+                    fsl.sample_partial_lse(h_g, W[p * Vg:(p + 1) * Vg], T_g, seed, step, p * Vg,
+                                           pv[p], pi[p], pl[p], workspace=ws)
             fsl.merge_lse(pv, pi, pl, T_g, seed, step, out=outs)
         # one step is G + 1 small launches: replay it as a captured graph so that
         # host-side call overhead does not stand in for device time
@@ -283,8 +287,10 @@ def main():
         gt = time_steps(torch, lambda i: graph.replay(), max(10, args.sweep_steps // 2), 5,
                         torch.cuda.current_stream(dev)) * 1e3
         del graph
-        plain = next((e["us_per_step"] for e in sweep if e["B"] == b), None)
+        plain = next((e.get("packed_us_per_step" if Wp is not None else "us_per_step")
+                      for e in sweep if e["B"] == b), None)
         grouped.append({"B": b, "groups": G, "us_per_step": round(gt, 2),
+                        "w_layout": "fragment order" if Wp is not None else "row-major",
                         "whole_vocabulary_us_per_step": plain})
         del h_g, T_g, pv, pi, pl, ws, outs
 

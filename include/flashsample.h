@@ -161,6 +161,16 @@ FS_API fs_status fs_sample_partial_lse(const void* h, const void* W, int32_t B, 
                                 int32_t* partial_idx, float* partial_lse, void* workspace,
                                 size_t workspace_bytes, void* stream);
 
+/* The same on fragment-order weights (fs_pack_weights, for this group's rows
+ * at this vocab_offset mod 4): W_packed in place of W, D % 32 == 0. */
+FS_API fs_status fs_sample_partial_lse_packed(const void* h, const void* W_packed, int32_t B,
+                                              int32_t D, int32_t V, int32_t vocab_offset,
+                                              const float* temperature, uint64_t seed,
+                                              uint64_t step, float* partial_val,
+                                              int32_t* partial_idx, float* partial_lse,
+                                              void* workspace, size_t workspace_bytes,
+                                              void* stream);
+
 /* Grouped merge: the categorical distribution factorises as
  * P(i) = P(G) P(i | G) with P(G) proportional to exp(LSE_G), and each
  * group's partial already holds a sample of P(i | G).

@@ -60,6 +60,8 @@ def lib():
         ("fs_merge", [vp, vp, i32, i32, vp, vp, vp], ctypes.c_int),
         ("fs_sample_partial_lse", [vp, vp, i32, i32, i32, i32, vp, u64, u64, vp, vp, vp, vp,
                                    sz, vp], ctypes.c_int),
+        ("fs_sample_partial_lse_packed", [vp, vp, i32, i32, i32, i32, vp, u64, u64, vp, vp, vp,
+                                          vp, sz, vp], ctypes.c_int),
         ("fs_merge_lse", [vp, vp, vp, i32, i32, vp, u64, u64, vp, vp, vp, vp], ctypes.c_int),
         ("fs_packed_weights_bytes", [i32, i32, i32], sz),
         ("fs_pack_weights", [vp, i32, i32, i32, vp, sz, vp], ctypes.c_int),
@@ -184,19 +186,29 @@ def sample_partial(h, W, temperature, seed, step, vocab_offset, partial_val, par
 
 
 def sample_partial_lse(h, W, temperature, seed, step, vocab_offset, partial_val, partial_idx,
-                       partial_lse, workspace=None):
+                       partial_lse, workspace=None, V=None):
     """One vocabulary group's per-row (max, global argmax) and log-sum-exp of the
-    scaled logits into partial_val / partial_idx / partial_lse (B each)."""
+    scaled logits into partial_val / partial_idx / partial_lse (B each).  W is the
+    group's row-major V x D rows, or (1-D, with V given) their fragment-order
+    copy from pack_weights at the same vocab_offset."""
     _req(partial_val, "partial_val", torch.float32, 1)
     _req(partial_idx, "partial_idx", torch.int32, 1)
     _req(partial_lse, "partial_lse", torch.float32, 1)
     _req(h, "h", torch.bfloat16, 2)
-    _req(W, "W", torch.bfloat16, 2)
+    packed = W.dim() == 1
+    _req(W, "W", torch.bfloat16, 1 if packed else 2)
     _req(temperature, "temperature", torch.float32, 1)
     B, D = h.shape
-    V, D2 = W.shape
-    if D2 != D:
-        raise ValueError(f"h is B x {D} but W is V x {D2}")
+    if packed:
+        if V is None:
+            raise ValueError("V is required with fragment-order W")
+        need = packed_weights_bytes(V, D, vocab_offset)
+        if need == 0 or W.numel() * 2 < need:
+            raise ValueError(f"W_packed holds {W.numel() * 2} bytes; {need} needed")
+    else:
+        V, D2 = W.shape
+        if D2 != D:
+            raise ValueError(f"h is B x {D} but W is V x {D2}")
     if not (temperature.shape[0] == partial_val.shape[0] == partial_idx.shape[0] ==
             partial_lse.shape[0] == B):
         raise ValueError("temperature and the partials must have B entries")
@@ -205,7 +217,8 @@ def sample_partial_lse(h, W, temperature, seed, step, vocab_offset, partial_val,
         raise ValueError("all tensors must be on one device")
     if workspace is None:
         workspace = alloc_workspace(workspace_bytes(B, D, V), h.device)
-    _check(lib().fs_sample_partial_lse(
+    fn = lib().fs_sample_partial_lse_packed if packed else lib().fs_sample_partial_lse
+    _check(fn(
         _ptr(h), _ptr(W), B, D, V, int(vocab_offset), _ptr(temperature),
         int(seed) & (2**64 - 1), int(step) & (2**64 - 1), _ptr(partial_val), _ptr(partial_idx),
         _ptr(partial_lse), _ptr(workspace), workspace.numel() * workspace.element_size(),

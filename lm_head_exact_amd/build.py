@@ -14,7 +14,7 @@ ROOT = os.path.dirname(HERE)
 CSRC = os.path.join(HERE, "csrc")
 BUILD = os.path.join(ROOT, "_build")
 LIB = os.path.join(HERE, "libflashsample.so")
-SOURCES = ["fs_configs_dma_a.hip", "fs_configs_dma_b.hip", "fs_configs_lds.hip",
+SOURCES = ["fs_configs_dma_a.hip", "fs_configs_dma_b.hip", "fs_configs_dma_ntl.hip", "fs_configs_lds.hip",
            "fs_configs_small.hip", "fs_fused.hip", "fs_api.hip", "fs_unfused.hip",
            "fs_online.hip", "fs_pack.hip"]
 

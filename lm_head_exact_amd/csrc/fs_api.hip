@@ -367,6 +367,17 @@ fs_status fs_sample_partial_lse(const void* h, const void* W, int32_t B, int32_t
                    "fs_sample_partial_lse");
 }
 
+fs_status fs_sample_partial_lse_packed(const void* h, const void* W_packed, int32_t B, int32_t D,
+                                       int32_t V, int32_t vocab_offset, const float* temperature,
+                                       uint64_t seed, uint64_t step, float* partial_val,
+                                       int32_t* partial_idx, float* partial_lse, void* workspace,
+                                       size_t workspace_bytes, void* stream) {
+  if (B > 0 && !partial_lse) return fail(FS_ERR_INVALID_ARG, "null pointer argument");
+  return run_fused(h, W_packed, B, D, V, vocab_offset, temperature, seed, step, partial_idx,
+                   partial_val, partial_lse, workspace, workspace_bytes, stream,
+                   "fs_sample_partial_lse_packed", true);
+}
+
 fs_status fs_merge_lse(const float* partial_val, const int32_t* partial_idx,
                        const float* partial_lse, int32_t P, int32_t B,
                        const float* temperature, uint64_t seed, uint64_t step,

@@ -19,19 +19,6 @@ int fused_configs_dma_b(const FusedConfig** out) {
       FS_DMAG(1, 16, 4, 64, 8, 3, 4, 2),
       FS_DMAG(1, 8, 4, 64, 8, 3, 4, 2),
       FS_DMAW(8, 4, 8, 64, 2, 3, 4, 2, 2),  // two batch groups of waves (WB = 2)
-      // non-temporal W loads: the twins the packed-W choice takes
-      FS_DMAN(2, 16, 8, 64, 4, 4, 4, 2),
-      FS_DMAN(2, 16, 8, 128, 4, 2, 4, 2),
-      FS_DMAPN(2, 16, 8, 128, 4, 2, 4, 2),
-      FS_DMAN(4, 4, 8, 64, 4, 3, 4, 2),
-      FS_DMAN(4, 8, 8, 64, 4, 3, 4, 2),
-      FS_DMAN(5, 4, 8, 64, 4, 3, 4, 2),
-      FS_DMAN(5, 8, 8, 64, 2, 3, 4, 2),
-      FS_DMAN(1, 4, 4, 64, 8, 3, 4, 2),
-      FS_DMAN(1, 8, 4, 64, 8, 3, 4, 2),
-      FS_DMAN(1, 16, 4, 64, 8, 3, 4, 2),
-      FS_DMAP(2, 16, 8, 64, 4, 4, 4, 2),
-      FS_DMAPN(2, 16, 8, 64, 4, 4, 4, 2),
   };
   *out = k;
   return static_cast<int>(sizeof(k) / sizeof(k[0]));

@@ -142,7 +142,7 @@ const std::vector<FusedConfig>& configs() {
   static const std::vector<FusedConfig> all = [] {
     std::vector<FusedConfig> v;
     for (auto part : {&fused_configs_small, &fused_configs_lds, &fused_configs_dma_a,
-                      &fused_configs_dma_b}) {
+                      &fused_configs_dma_b, &fused_configs_dma_ntl}) {
       const FusedConfig* k = nullptr;
       const int n = part(&k);
       v.insert(v.end(), k, k + n);

@@ -40,6 +40,7 @@ int fused_configs_small(const FusedConfig** out);
 int fused_configs_lds(const FusedConfig** out);
 int fused_configs_dma_a(const FusedConfig** out);
 int fused_configs_dma_b(const FusedConfig** out);
+int fused_configs_dma_ntl(const FusedConfig** out);
 
 // ---- fused sampler (fs_fused.hip) ----
 int num_fused_configs();

@@ -374,12 +374,17 @@ hipError_t launch_cfg(SampleArgs& a, hipStream_t stream) {
   const dim3 block(Loop::NW * kWave);
   if (a.w_packed) {
     if constexpr (reads_packed_w<Loop>::value) {
-      if (a.part_lse != nullptr) return hipErrorInvalidValue;
       if (smem > 0) {
-        static const hipError_t attr = allow_smem(&fused_sample_kernel<Loop, false, true>, smem);
+        static const hipError_t attr = [] {
+          const hipError_t e = allow_smem(&fused_sample_kernel<Loop, false, true>, smem);
+          return e != hipSuccess ? e : allow_smem(&fused_sample_kernel<Loop, true, true>, smem);
+        }();
         if (attr != hipSuccess) return attr;
       }
-      fused_sample_kernel<Loop, false, true><<<grid, block, smem, stream>>>(a);
+      if (a.part_lse == nullptr)
+        fused_sample_kernel<Loop, false, true><<<grid, block, smem, stream>>>(a);
+      else
+        fused_sample_kernel<Loop, true, true><<<grid, block, smem, stream>>>(a);
       return hipGetLastError();
     } else {
       return hipErrorInvalidValue;
@@ -432,7 +437,7 @@ struct Persist {
   }
   static hipError_t launch(SampleArgs& a, hipStream_t stream) {
     if (!supports(a.B, a.D)) return hipErrorInvalidValue;
-    if (a.w_packed) return a.part_lse == nullptr ? go<false, true>(a, stream) : hipErrorInvalidValue;
+    if (a.w_packed) return a.part_lse == nullptr ? go<false, true>(a, stream) : go<true, true>(a, stream);
     return a.part_lse == nullptr ? go<false>(a, stream) : go<true>(a, stream);
   }
 };

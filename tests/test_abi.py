@@ -258,3 +258,17 @@ def test_online_packed_argument_errors(L):
     assert call(_cuts(0, 512, 1000), D=264) == bd.FS_ERR_INVALID_ARG  # D % 32 != 0
     assert call(_cuts(0, 512, 999)) == bd.FS_ERR_INVALID_ARG          # does not end at V
     assert call(_cuts(0, 512, 1000), wsb=16) == bd.FS_ERR_WORKSPACE
+
+
+def test_partial_lse_packed_argument_errors(L):
+    def call(**kw):
+        a = dict(h=ALIGNED, W=ALIGNED, B=4, D=256, V=1000, off=0, T=ALIGNED, pv=ALIGNED,
+                 pi=ALIGNED, pl=ALIGNED, ws=WS_ALIGNED, wsb=1 << 30)
+        a.update(kw)
+        return L.fs_sample_partial_lse_packed(a["h"], a["W"], a["B"], a["D"], a["V"], a["off"],
+                                              a["T"], 1, 2, a["pv"], a["pi"], a["pl"], a["ws"],
+                                              a["wsb"], None)
+    assert call(D=264) == bd.FS_ERR_INVALID_ARG
+    assert call(pl=None) == bd.FS_ERR_INVALID_ARG
+    assert call(wsb=16) == bd.FS_ERR_WORKSPACE
+    assert call(B=0, h=None, W=None, T=None, pv=None, pi=None, pl=None, ws=None) == bd.FS_OK

@@ -20,7 +20,7 @@ import pytest
 
 ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
 CSRC = os.path.join(ROOT, "lm_head_exact_amd", "csrc")
-DMA_UNITS = ("fs_configs_dma_a.hip", "fs_configs_dma_b.hip")
+DMA_UNITS = ("fs_configs_dma_a.hip", "fs_configs_dma_b.hip", "fs_configs_dma_ntl.hip")
 
 pytestmark = pytest.mark.skipif(shutil.which("hipcc") is None and
                                 not os.path.exists("/opt/rocm/bin/hipcc"),

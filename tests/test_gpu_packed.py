@@ -151,3 +151,35 @@ def test_unsupported_configuration_is_an_error():
     with pytest.raises(fsl.FlashSampleError) as e:
         fsl.sample_packed(h.to(DEV), Wp, V, T.to(DEV), 1, 1)
     assert e.value.status == fsl.binding.FS_ERR_UNSUPPORTED
+
+
+@pytest.mark.parametrize("cfg", range(_num_configs()))
+def test_every_packed_config_partial_lse_equals_row_major(cfg):
+    """The grouped sampler's per-group kernel on fragment-order W: (val, idx,
+    lse) bit-identical to the row-major call in the same configuration."""
+    if not _packed_capable(cfg):
+        pytest.skip("configuration without a packed-W kernel")
+    fsl.force_config(cfg)
+    ran = 0
+    for B, D, V, off in [(37, 256, 1531, 6), (4, 256, 1000, 0), (300, 128, 700, 48097)]:
+        h, W, T = _rand(B, D, V, seed=2 * B + V)
+        outs = []
+        try:
+            for Wx, kw in ((W.to(DEV), {}), (fsl.pack_weights(W.to(DEV), off), {"V": V})):
+                o = (torch.empty(B, dtype=torch.float32, device=DEV),
+                     torch.empty(B, dtype=torch.int32, device=DEV),
+                     torch.empty(B, dtype=torch.float32, device=DEV))
+                fsl.sample_partial_lse(h.to(DEV), Wx, T.to(DEV), 7, 2, off, *o, **kw)
+                outs.append([to_host(t) for t in o])
+        except fsl.FlashSampleError as e:
+            if e.status == fsl.binding.FS_ERR_UNSUPPORTED:
+                continue
+            raise
+        torch.cuda.synchronize()
+        (v0, i0, l0), (v1, i1, l1) = outs
+        assert np.array_equal(i0, i1), fsl.config_name(cfg)
+        assert np.array_equal(v0.view(np.uint32), v1.view(np.uint32)), fsl.config_name(cfg)
+        assert np.array_equal(l0.view(np.uint32), l1.view(np.uint32)), fsl.config_name(cfg)
+        ran += 1
+    if ran == 0:
+        pytest.skip("configuration supports none of the test shapes")
