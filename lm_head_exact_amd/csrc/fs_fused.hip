@@ -240,6 +240,12 @@ static int auto_config_shape(int32_t B, int32_t D, int32_t V, bool packed) {
   static const int persist[] = {config_id("persist_nt1_nw8_ks16_p8"),
                                 config_id("persist_nt2_nw8_ks16_p8"),
                                 config_id("persist_nt1_nw8_ks32_p8")};
+  // on packed W (non-temporal loads) the load ring depth that times best per
+  // batch tile (Llama-3 head: B = 1 156.6 against 158.8 us with 16 steps
+  // instead of 8; B = 32 162.5 against 166.7 us with 4)
+  static const int persist_packed[] = {config_id("persist_nt1_nw8_ks16_p16_ntl1"),
+                                       config_id("persist_nt2_nw8_ks16_p4_ntl1"),
+                                       config_id("persist_nt1_nw8_ks32_p8_ntl1")};
   static const int ksplit = config_id("ksplit_mr1_nt1_nw4_p8_ntl0");
   // batch-tiled loops: the DMA-staged loop (one 8-wave block per CU) when its
   // grid fills the CUs; for a short vocabulary the same loop on 64-row blocks
@@ -262,7 +268,7 @@ static int auto_config_shape(int32_t B, int32_t D, int32_t V, bool packed) {
   static const int lds_narrow = config_id("lds_mr2_nt8_nw4_kc64_p8_wb1_br4");
   static const int stream_small = config_id("stream_mr4_nt1_nw4_p4_ntl0");
   static const int stream_big = config_id("stream_mr2_nt4_nw4_p4_ntl0");
-  for (int id : persist)
+  for (int id : packed ? persist_packed : persist)
     if (fused_config_supports(id, B, D)) return id;
   // (the K-split loop reads row-major W only: packed W goes on to the DMA loop)
   if (!packed && B <= 8 && fused_config_supports(ksplit, B, D)) return ksplit;
