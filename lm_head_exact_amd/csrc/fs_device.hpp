@@ -146,6 +146,31 @@ struct ArgMax {
   }
 };
 
+// Lane-strided argmax over P pairs (element p at o(p)), with the loads of
+// kMergeUnroll strides issued before any comparison so that they are in
+// flight together (the pairs were just written and sit in L2; one at a time
+// they would cost one round trip each).  The comparator orders by value,
+// then id, so the push order does not change the result.
+constexpr int kMergeUnroll = 8;
+template <class Off>
+__device__ __forceinline__ void strided_argmax(const float* __restrict__ val,
+                                               const int32_t* __restrict__ idx, int32_t P,
+                                               int lane, Off o, ArgMax& m) {
+  for (int p0 = lane; p0 < P; p0 += kWave * kMergeUnroll) {
+    float v[kMergeUnroll];
+    int32_t i[kMergeUnroll];
+#pragma unroll
+    for (int u = 0; u < kMergeUnroll; ++u) {
+      const int p = p0 + u * kWave;
+      const bool in = p < P;
+      v[u] = in ? val[o(p)] : -__builtin_inff();
+      i[u] = in ? idx[o(p)] : 0x7FFFFFFF;
+    }
+#pragma unroll
+    for (int u = 0; u < kMergeUnroll; ++u) m.push(v[u], i[u]);
+  }
+}
+
 // ---------------------------------------------------------------------------
 // Running log-sum-exp, log sum_i exp(t_i), of a stream of scaled logits t_i,
 // kept as (m, s) with m the running maximum and s = sum_i exp(t_i - m)

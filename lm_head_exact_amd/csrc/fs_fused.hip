@@ -22,10 +22,8 @@ __global__ __launch_bounds__(256) void merge_kernel(const float* __restrict__ va
   if (b >= B) return;  // uniform per wave
   ArgMax m;
   m.init();
-  for (int p = lane; p < P; p += kWave) {
-    const int64_t o = p * stride_p + b * stride_b;
-    m.push(val[o], idx[o]);
-  }
+  strided_argmax(val, idx, P, lane,
+                 [&](int p) FS_INLINE { return p * stride_p + b * stride_b; }, m);
 #pragma unroll
   for (int mask = 32; mask >= 1; mask >>= 1) m.xor_reduce(mask);
   if (lane == 0) {

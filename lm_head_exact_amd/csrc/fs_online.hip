@@ -123,10 +123,8 @@ __global__ __launch_bounds__(256) void online_step_kernel(
     m.v = out_val[b];
     m.i = out_ids[b];
   }
-  for (int t = lane; t < S; t += kWave) {
-    const int64_t o = static_cast<int64_t>(b) * S + t;
-    m.push(part_val[o], part_idx[o]);
-  }
+  strided_argmax(part_val, part_idx, S, lane,
+                 [&](int t) FS_INLINE { return static_cast<int64_t>(b) * S + t; }, m);
 #pragma unroll
   for (int mask = 32; mask >= 1; mask >>= 1) m.xor_reduce(mask);
   if (lane == 0) {
