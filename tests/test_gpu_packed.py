@@ -214,3 +214,25 @@ def test_captured_graph_replays_match_eager():
         assert junk.isfinite()
         for a, b in zip(out, ref):
             assert torch.equal(a, b), f"replay {r}"
+
+
+@pytest.mark.parametrize("B,D,V,off", [
+    (4096, 256, 600, 0),                 # sixteen 256-row batch tiles
+    (3, 256, 2000, 2**31 - 1 - 2000),    # the vocabulary ends at id 2^31 - 2
+    (1, 256, 1, 2**31 - 2),              # one id (one padded group), near the top of the ids
+])
+def test_maximum_sizes(B, D, V, off):
+    """Extremes of the argument ranges on fragment-order W: against the
+    oracle, and bit-identical to the row-major call in the same configuration."""
+    h, W, T = _rand(B, D, V, seed=B + V)
+    hd, Wd, Td = h.to(DEV), W.to(DEV), T.to(DEV)
+    Wp = fsl.pack_weights(Wd, off)
+    assert Wp.numel() == ((V + off % 4 + 15) // 16) * 16 * D
+    ids_p, val_p = fsl.sample_packed(hd, Wp, V, Td, 123, 456, off)
+    fsl.force_config(fsl.selected_config(B, D, V, packed=True))
+    ids, val = fsl.sample(hd, Wd, Td, 123, 456, off)
+    torch.cuda.synchronize()
+    assert torch.equal(ids_p, ids) and torch.equal(val_p.view(torch.int32), val.view(torch.int32))
+    rows = None if B <= 64 else sample_rows(B, k=24, seed=1)
+    check_rows(wl.bf16_bits(h), wl.bf16_bits(W), T.numpy(), 123, 456, off, to_host(ids_p),
+               to_host(val_p), rows=rows, label=f"packed max B{B} V{V} off{off}")
