@@ -90,7 +90,7 @@ __device__ __forceinline__ uint32_t pick_word(u32x4 w, uint32_t i) {
 // difference and an absolute error in log2 becomes a large relative error in
 // -ln u, which the outer log turns into an absolute error in g.  Both u and
 // v = 1 - u = (2^24 - 1 - 2k) 2^-24 are exact in fp32, so for v <= 1/16 the
-// series -ln(1 - v) = v + v^2/2 + ... + v^7/7 (truncation below 5e-10
+// series -ln(1 - v) = v + v^2/2 + ... + v^5/5 (truncation below 1.6e-7
 // relative) is used instead.  Elsewhere |ln u| >= 0.06 and the hardware log
 // is used directly.  The device values are checked against the fp64 oracle
 // on all 2^23 grid points.
