@@ -309,3 +309,25 @@ def test_packed_full_size_confident_and_random(B):
         del W
         assert np.all(used == (1 if kind == "confident" else 8)), used
         check_rows(hb, Wb, Tb, seed, step, 0, ids, val, rows=rows, label=f"packed {kind} B={B}")
+
+
+def test_poisoned_workspace():
+    """Workspace contents on entry are ignored: a 0xFF-filled workspace (as
+    partials, norms, flags and live counts) gives the same result as a fresh
+    one, on row-major and on packed W."""
+    B, D, V, c0 = 40, 128, 2400, 320
+    h, W = _aligned(B, D, V, c0, seed=6, norm=8.0)
+    T = torch.as_tensor(np.resize(np.asarray(TEMPS, np.float32), B)).to(DEV)
+    hd, Wd = h.to(DEV), W.to(DEV)
+    cuts = [0, c0, 896, V]
+    later = fsl.online_bounds(Wd, cuts)
+    Wp = fsl.pack_weights(Wd)
+    for Wx, kw in ((Wd, {}), (Wp, {"V": V})):
+        ref = [t.clone() for t in fsl.sample_online(hd, Wx, T, 2, 3, cuts, later, **kw)]
+        ws = fsl.alloc_workspace(fsl.online_workspace_bytes(B, D, V, 3), DEV)
+        ws.fill_(0xFF)
+        got = fsl.sample_online(hd, Wx, T, 2, 3, cuts, later, workspace=ws, **kw)
+        torch.cuda.synchronize()
+        for a, b in zip(got, ref):
+            assert torch.equal(a, b)
+        assert (ref[2] == 1).any() and (ref[2] > 1).any()

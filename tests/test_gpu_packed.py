@@ -236,3 +236,18 @@ def test_maximum_sizes(B, D, V, off):
     rows = None if B <= 64 else sample_rows(B, k=24, seed=1)
     check_rows(wl.bf16_bits(h), wl.bf16_bits(W), T.numpy(), 123, 456, off, to_host(ids_p),
                to_host(val_p), rows=rows, label=f"packed max B{B} V{V} off{off}")
+
+
+def test_poisoned_workspace():
+    """A 0xFF-filled workspace gives the same result as a fresh one."""
+    B, D, V = 300, 256, 1531
+    h, W, T = _rand(B, D, V, seed=12)
+    hd, Td = h.to(DEV), T.to(DEV)
+    Wp = fsl.pack_weights(W.to(DEV), 1)
+    ref = [t.clone() for t in fsl.sample_packed(hd, Wp, V, Td, 5, 5, 1)]
+    ws = fsl.alloc_workspace(fsl.workspace_bytes(B, D, V), DEV)
+    ws.fill_(0xFF)
+    got = fsl.sample_packed(hd, Wp, V, Td, 5, 5, 1, workspace=ws)
+    torch.cuda.synchronize()
+    for a, b in zip(got, ref):
+        assert torch.equal(a, b)
