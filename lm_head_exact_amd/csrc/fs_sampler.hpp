@@ -21,6 +21,7 @@
 // (fs_configs_*.hip) so that they compile in parallel.
 #pragma once
 
+#include <atomic>
 #include <type_traits>
 
 #include "fs_internal.hpp"
@@ -402,23 +403,32 @@ bool supports_cfg(int32_t B, int32_t D) {
   return Loop::supports(D) && static_cast<size_t>(B) * D * 2 <= Loop::kMaxHBytes;
 }
 
+// Per-device results of one kernel's occupancy query (0: not yet known).
+// Each kernel keeps its own: kernels of one signature share a pointer type,
+// so a cache keyed on that type would hand one kernel's answer to another.
+struct OccupancyCache {
+  static constexpr int kMaxDevices = 64;
+  std::atomic<int> blocks[kMaxDevices];
+};
+
 // Blocks of `kernel` that fit on one CU, times the CU count of the current
-// device (cached per device).
+// device, cached per device in `cache`.
 template <class Kernel>
-int resident_blocks(Kernel kernel, int threads, size_t smem) {
-  static int cached_dev = -1, cached = 0;
+int resident_blocks(Kernel kernel, int threads, size_t smem, OccupancyCache& cache) {
   int dev = 0;
   if (hipGetDevice(&dev) != hipSuccess) return 0;
-  if (dev != cached_dev) {
-    int cus = 0, per_cu = 0;
-    if (hipDeviceGetAttribute(&cus, hipDeviceAttributeMultiprocessorCount, dev) != hipSuccess ||
-        hipOccupancyMaxActiveBlocksPerMultiprocessor(&per_cu, kernel, threads, smem) !=
-            hipSuccess)
-      return 0;
-    cached = cus * (per_cu > 0 ? per_cu : 1);
-    cached_dev = dev;
+  const bool cacheable = dev >= 0 && dev < OccupancyCache::kMaxDevices;
+  if (cacheable) {
+    const int known = cache.blocks[dev].load(std::memory_order_relaxed);
+    if (known > 0) return known;
   }
-  return cached;
+  int cus = 0, per_cu = 0;
+  if (hipDeviceGetAttribute(&cus, hipDeviceAttributeMultiprocessorCount, dev) != hipSuccess ||
+      hipOccupancyMaxActiveBlocksPerMultiprocessor(&per_cu, kernel, threads, smem) != hipSuccess)
+    return 0;
+  const int n = cus * (per_cu > 0 ? per_cu : 1);
+  if (cacheable) cache.blocks[dev].store(n, std::memory_order_relaxed);
+  return n;
 }
 
 template <int NT, int NW, int KS, int P, bool NTL = false>
@@ -428,7 +438,8 @@ struct Persist {
   template <bool LSE, bool PACKED = false>
   static hipError_t go(SampleArgs& a, hipStream_t stream) {
     const auto kernel = persist_sample_kernel<NT, NW, KS, P, LSE, PACKED, NTL>;
-    const int slots = resident_blocks(kernel, NW * kWave, kSmemBytes);
+    static OccupancyCache cache;  // one per kernel instantiation
+    const int slots = resident_blocks(kernel, NW * kWave, kSmemBytes, cache);
     if (slots <= 0) return hipErrorInvalidDevice;
     const int ngroups = (a.V + (a.vocab_offset & 3) + 15) / 16;
     a.S = ngroups < slots ? ngroups : slots;
