@@ -2,6 +2,7 @@
 // choice, the merge kernels (tile partials, shard partials, grouped
 // partials) and the noise diagnostics.  The sampler kernels themselves are
 // in fs_sampler.hpp, instantiated by fs_configs_*.hip.
+#include <atomic>
 #include <cstring>
 #include <string>
 #include <vector>
@@ -182,18 +183,23 @@ bool fused_config_supports(int id, int32_t B, int32_t D) {
 }
 
 namespace {
+// CU count of the current device, cached per device (0 until known; callers
+// on several threads may race to fill an entry, with the same value).
 int device_cus() {
-  static int cached_dev = -1, cached = 0;
+  constexpr int kMaxDevices = 64;
+  static std::atomic<int> cached[kMaxDevices];
   int dev = 0;
   if (hipGetDevice(&dev) != hipSuccess) return 0;
-  if (dev != cached_dev) {
-    int cus = 0;
-    if (hipDeviceGetAttribute(&cus, hipDeviceAttributeMultiprocessorCount, dev) != hipSuccess)
-      return 0;
-    cached = cus;
-    cached_dev = dev;
+  const bool cacheable = dev >= 0 && dev < kMaxDevices;
+  if (cacheable) {
+    const int known = cached[dev].load(std::memory_order_relaxed);
+    if (known > 0) return known;
   }
-  return cached;
+  int cus = 0;
+  if (hipDeviceGetAttribute(&cus, hipDeviceAttributeMultiprocessorCount, dev) != hipSuccess)
+    return 0;
+  if (cacheable) cached[dev].store(cus, std::memory_order_relaxed);
+  return cus;
 }
 
 // Share of CU slots busy over the whole grid of a configuration that runs one
