@@ -21,8 +21,9 @@ int fused_configs_small(const FusedConfig** out) {
       FS_PERSISTN(1, 8, 16, 8),
       FS_PERSISTN(2, 8, 16, 8),
       FS_PERSISTN(1, 8, 32, 8),
-      FS_PERSISTN(1, 8, 16, 16),  // packed W, B <= 16
+      FS_PERSISTN(1, 8, 16, 16),  // packed W: tuning alternative
       FS_PERSISTN(2, 8, 16, 4),   // packed W, B <= 32
+      FS_PERSISTN(1, 16, 8, 4),   // packed W, B <= 16
   };
   *out = k;
   return static_cast<int>(sizeof(k) / sizeof(k[0]));

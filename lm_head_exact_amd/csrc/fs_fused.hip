@@ -244,10 +244,11 @@ static int auto_config_shape(int32_t B, int32_t D, int32_t V, bool packed) {
   static const int persist[] = {config_id("persist_nt1_nw8_ks16_p8"),
                                 config_id("persist_nt2_nw8_ks16_p8"),
                                 config_id("persist_nt1_nw8_ks32_p8")};
-  // on packed W (non-temporal loads) the load ring depth that times best per
-  // batch tile (Llama-3 head: B = 1 156.6 against 158.8 us with 16 steps
-  // instead of 8; B = 32 162.5 against 166.7 us with 4)
-  static const int persist_packed[] = {config_id("persist_nt1_nw8_ks16_p16_ntl1"),
+  // on packed W (non-temporal loads) the block shape and load ring depth
+  // that time best per batch tile (Llama-3 head: B = 1 156 us with 16 waves
+  // of 8 k-steps and a 4-step ring, against 159 us with 8 waves and 16 steps
+  // and 159 with 8 and 8; B = 32 162.5 against 166.7 us with a 4-step ring)
+  static const int persist_packed[] = {config_id("persist_nt1_nw16_ks8_p4_ntl1"),
                                        config_id("persist_nt2_nw8_ks16_p4_ntl1"),
                                        config_id("persist_nt1_nw8_ks32_p8_ntl1")};
   static const int ksplit = config_id("ksplit_mr1_nt1_nw4_p8_ntl0");
