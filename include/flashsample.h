@@ -291,8 +291,10 @@ FS_API int32_t fs_selected_config_packed(int32_t B, int32_t D, int32_t V);
 
 /* Profiling of the fused kernel.  fs_profile_enable(capacity) creates
  * 2 * capacity HIP events (outside any sampling call); while enabled, each of
- * the next `capacity` fs_sample / fs_sample_partial calls records one event
- * before and one after its fused-kernel launch, on the caller's stream.
+ * the next `capacity` fs_sample / fs_sample_partial / fs_sample_partial_lse
+ * calls (and their _packed forms) records one event before and one after its
+ * fused-kernel launch, on the caller's stream (the online sampler's chunk
+ * launches are not recorded).
  * fs_profile_read waits for the recorded events, returns the number of timed
  * launches and the sum, minimum and maximum of their durations in
  * milliseconds (any output may be NULL), and re-arms the recorder.
