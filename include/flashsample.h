@@ -242,8 +242,13 @@ FS_API fs_status fs_sample_online(const void* h, const void* W, int32_t B, int32
 /* The same on fragment-order weights (fs_pack_weights at the same
  * vocab_offset mod 4): W_packed in place of W, every chunk start cuts[c]
  * (0 < c < n_chunks) a multiple of 16, D % 32 == 0 (FS_ERR_INVALID_ARG
- * otherwise).  later_norm comes from fs_online_bounds on the row-major W.
- * Results as fs_sample_packed over the whole W. */
+ * otherwise).  later_norm comes from fs_online_bounds on the row-major W or
+ * from fs_online_bounds_packed on W_packed (same values up to fp64 summation
+ * order).  Results as fs_sample_packed over the whole W. */
+FS_API fs_status fs_online_bounds_packed(const void* W_packed, int32_t V, int32_t D,
+                                         int32_t vocab_offset, const int32_t* cuts,
+                                         int32_t n_chunks, double* later_norm, void* workspace,
+                                         size_t workspace_bytes, void* stream);
 FS_API fs_status fs_sample_online_packed(const void* h, const void* W_packed, int32_t B,
                                          int32_t D, int32_t V, int32_t vocab_offset,
                                          const float* temperature, uint64_t seed, uint64_t step,

@@ -69,6 +69,7 @@ def lib():
         ("fs_online_bounds_workspace_bytes", [i32, i32], sz),
         ("fs_online_workspace_bytes", [i32, i32, i32, i32], sz),
         ("fs_online_bounds", [vp, i32, i32, vp, i32, vp, vp, sz, vp], ctypes.c_int),
+        ("fs_online_bounds_packed", [vp, i32, i32, i32, vp, i32, vp, vp, sz, vp], ctypes.c_int),
         ("fs_sample_online", [vp, vp, i32, i32, i32, i32, vp, u64, u64, vp, i32, vp, vp, vp,
                               vp, vp, sz, vp], ctypes.c_int),
         ("fs_sample_online_packed", [vp, vp, i32, i32, i32, i32, vp, u64, u64, vp, i32, vp, vp,
@@ -335,18 +336,34 @@ def _host_cuts(cuts):
     return (ctypes.c_int32 * len(c))(*c), len(c) - 1
 
 
-def online_bounds(W: torch.Tensor, cuts, workspace: Optional[torch.Tensor] = None):
+def online_bounds(W: torch.Tensor, cuts, workspace: Optional[torch.Tensor] = None,
+                  V: Optional[int] = None, D: Optional[int] = None, vocab_offset: int = 0):
     """later_norm (fp64 [n_chunks], device) for the online sampler over the
-    chunks W[cuts[c]:cuts[c+1]]: the largest row norm after each chunk."""
-    _req(W, "W", torch.bfloat16, 2)
-    V, D = W.shape
+    chunks W[cuts[c]:cuts[c+1]]: the largest row norm after each chunk.  W is
+    the row-major V x D matrix, or (1-D, with V and D given) its fragment-order
+    copy from pack_weights at vocab_offset."""
+    packed = W.dim() == 1
+    _req(W, "W", torch.bfloat16, 1 if packed else 2)
+    if packed:
+        if V is None or D is None:
+            raise ValueError("V and D are required with fragment-order W")
+        need = packed_weights_bytes(V, D, vocab_offset)
+        if need == 0 or W.numel() * 2 < need:
+            raise ValueError(f"W_packed holds {W.numel() * 2} bytes; {need} needed")
+    else:
+        V, D = W.shape
     arr, n = _host_cuts(cuts)
     later = torch.empty(n, dtype=torch.float64, device=W.device)
     if workspace is None:
         workspace = alloc_workspace(int(lib().fs_online_bounds_workspace_bytes(V, n)), W.device)
-    _check(lib().fs_online_bounds(_ptr(W), V, D, arr, n, _ptr(later), _ptr(workspace),
-                                  workspace.numel() * workspace.element_size(),
-                                  _stream(W.device)))
+    nbytes = workspace.numel() * workspace.element_size()
+    if packed:
+        _check(lib().fs_online_bounds_packed(_ptr(W), V, D, int(vocab_offset), arr, n,
+                                             _ptr(later), _ptr(workspace), nbytes,
+                                             _stream(W.device)))
+    else:
+        _check(lib().fs_online_bounds(_ptr(W), V, D, arr, n, _ptr(later), _ptr(workspace), nbytes,
+                                      _stream(W.device)))
     return later
 
 

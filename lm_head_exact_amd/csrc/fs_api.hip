@@ -292,6 +292,41 @@ static fs_status run_online(const void* h, const void* W, int32_t B, int32_t D, 
   return FS_OK;
 }
 
+// Shared body of fs_online_bounds / fs_online_bounds_packed.
+static fs_status run_online_bounds(const void* W, int32_t V, int32_t D, int32_t vocab_offset,
+                                   const int32_t* cuts, int32_t n_chunks, double* later_norm,
+                                   void* workspace, size_t workspace_bytes, void* stream,
+                                   bool packed) {
+  fs_status s = check_shape(1, D, V, vocab_offset);
+  if (s != FS_OK) return s;
+  if (packed && D % 32 != 0)
+    return fail(FS_ERR_INVALID_ARG, "fs_online_bounds_packed: D must be a multiple of 32 (got %d)", D);
+  if ((s = check_cuts(cuts, n_chunks, V, "fs_online_bounds")) != FS_OK) return s;
+  if (!W || !later_norm || !workspace) return fail(FS_ERR_INVALID_ARG, "null pointer argument");
+  if (!aligned(W, 16)) return fail(FS_ERR_INVALID_ARG, "W must be 16-byte aligned");
+  if (!aligned(later_norm, 8)) return fail(FS_ERR_INVALID_ARG, "later_norm must be 8-byte aligned");
+  if (!aligned(workspace, 256)) return fail(FS_ERR_INVALID_ARG, "workspace must be 256-byte aligned");
+  const size_t need = online_bounds_workspace(V, n_chunks);
+  if (workspace_bytes < need)
+    return fail(FS_ERR_WORKSPACE, "fs_online_bounds: workspace of %zu bytes is below the %zu required",
+                workspace_bytes, need);
+  const hipStream_t st = static_cast<hipStream_t>(stream);
+  double* norms = static_cast<double*>(workspace);
+  double* chunk_max = reinterpret_cast<double*>(static_cast<char*>(workspace) +
+                                                fs::round_up(sizeof(double) * V, 256));
+  hipError_t e = packed ? fs::launch_packed_row_norms(static_cast<const __bf16*>(W), V, D,
+                                                       vocab_offset, norms, st)
+                        : fs::launch_row_norms(static_cast<const __bf16*>(W), V, D, norms, st);
+  if (e != hipSuccess) return hip_fail(e, "row norm launch");
+  for (int32_t c = 0; c < n_chunks; ++c) {
+    e = fs::launch_max_reduce(norms + cuts[c], cuts[c + 1] - cuts[c], chunk_max + c, st);
+    if (e != hipSuccess) return hip_fail(e, "chunk norm launch");
+  }
+  e = fs::launch_suffix_max(chunk_max, n_chunks, later_norm, st);
+  if (e != hipSuccess) return hip_fail(e, "suffix max launch");
+  return FS_OK;
+}
+
 }  // namespace
 
 extern "C" {
@@ -414,30 +449,16 @@ size_t fs_online_workspace_bytes(int32_t B, int32_t D, int32_t V, int32_t n_chun
 fs_status fs_online_bounds(const void* W, int32_t V, int32_t D, const int32_t* cuts,
                            int32_t n_chunks, double* later_norm, void* workspace,
                            size_t workspace_bytes, void* stream) {
-  fs_status s = check_shape(1, D, V, 0);
-  if (s != FS_OK) return s;
-  if ((s = check_cuts(cuts, n_chunks, V, "fs_online_bounds")) != FS_OK) return s;
-  if (!W || !later_norm || !workspace) return fail(FS_ERR_INVALID_ARG, "null pointer argument");
-  if (!aligned(W, 16)) return fail(FS_ERR_INVALID_ARG, "W must be 16-byte aligned");
-  if (!aligned(later_norm, 8)) return fail(FS_ERR_INVALID_ARG, "later_norm must be 8-byte aligned");
-  if (!aligned(workspace, 256)) return fail(FS_ERR_INVALID_ARG, "workspace must be 256-byte aligned");
-  const size_t need = online_bounds_workspace(V, n_chunks);
-  if (workspace_bytes < need)
-    return fail(FS_ERR_WORKSPACE, "fs_online_bounds: workspace of %zu bytes is below the %zu required",
-                workspace_bytes, need);
-  const hipStream_t st = static_cast<hipStream_t>(stream);
-  double* norms = static_cast<double*>(workspace);
-  double* chunk_max = reinterpret_cast<double*>(static_cast<char*>(workspace) +
-                                                fs::round_up(sizeof(double) * V, 256));
-  hipError_t e = fs::launch_row_norms(static_cast<const __bf16*>(W), V, D, norms, st);
-  if (e != hipSuccess) return hip_fail(e, "row norm launch");
-  for (int32_t c = 0; c < n_chunks; ++c) {
-    e = fs::launch_max_reduce(norms + cuts[c], cuts[c + 1] - cuts[c], chunk_max + c, st);
-    if (e != hipSuccess) return hip_fail(e, "chunk norm launch");
-  }
-  e = fs::launch_suffix_max(chunk_max, n_chunks, later_norm, st);
-  if (e != hipSuccess) return hip_fail(e, "suffix max launch");
-  return FS_OK;
+  return run_online_bounds(W, V, D, 0, cuts, n_chunks, later_norm, workspace, workspace_bytes,
+                           stream, false);
+}
+
+fs_status fs_online_bounds_packed(const void* W_packed, int32_t V, int32_t D,
+                                  int32_t vocab_offset, const int32_t* cuts, int32_t n_chunks,
+                                  double* later_norm, void* workspace, size_t workspace_bytes,
+                                  void* stream) {
+  return run_online_bounds(W_packed, V, D, vocab_offset, cuts, n_chunks, later_norm, workspace,
+                           workspace_bytes, stream, true);
 }
 
 fs_status fs_sample_online(const void* h, const void* W, int32_t B, int32_t D, int32_t V,

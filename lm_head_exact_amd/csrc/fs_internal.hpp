@@ -78,6 +78,9 @@ hipError_t launch_merge_groups_lse(const float* val, const int32_t* idx, const f
 // Euclidean norm of each of the n rows of X (bf16, row length D), fp64.
 hipError_t launch_row_norms(const __bf16* X, int32_t n, int32_t D, double* out,
                             hipStream_t stream);
+// The same from fragment-order W (packed for vocab_offset mod 4).
+hipError_t launch_packed_row_norms(const __bf16* Wp, int32_t V, int32_t D, int32_t vocab_offset,
+                                   double* out, hipStream_t stream);
 // out[0] = max of x[0 .. n).
 hipError_t launch_max_reduce(const double* x, int32_t n, double* out, hipStream_t stream);
 // later[c] = max(chunk_max[c+1 .. n_chunks)), later[n_chunks - 1] = 0.

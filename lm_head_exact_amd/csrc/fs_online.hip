@@ -57,6 +57,37 @@ __global__ __launch_bounds__(256) void row_norms_kernel(const __bf16* __restrict
   if (lane == 0) out[r] = nrm;
 }
 
+// One wave per 16-row group of fragment-order W (packed_frag's layout): lane l
+// sums the squares of its 16-byte pieces over the group's k-steps (1 KB
+// contiguous per step), and the four lanes l, l ^ 16, l ^ 32, l ^ 48 that hold
+// the same row combine their sums; rows outside [0, V) (padding) are skipped.
+__global__ __launch_bounds__(256) void packed_row_norms_kernel(const __bf16* __restrict__ Wp,
+                                                               int32_t V, int32_t D, int32_t shift,
+                                                               int64_t groups,
+                                                               double* __restrict__ out) {
+  const int lane = threadIdx.x & (kWave - 1);
+  const int64_t g = blockIdx.x * 4ll + (threadIdx.x >> 6);
+  if (g >= groups) return;  // uniform per wave
+  const int ksteps = D / 32;
+  const __bf16* p = Wp + (g * ksteps * kWave + lane) * 8;
+  double s = 0.0;
+  for (int k = 0; k < ksteps; ++k) {
+    const uint4 q = *reinterpret_cast<const uint4*>(p + static_cast<int64_t>(k) * kWave * 8);
+    const uint32_t w[4] = {q.x, q.y, q.z, q.w};
+#pragma unroll
+    for (int j = 0; j < 4; ++j) {
+      const double lo = __uint_as_float(w[j] << 16);
+      const double hi = __uint_as_float(w[j] & 0xFFFF0000u);
+      s += lo * lo;
+      s += hi * hi;
+    }
+  }
+  s += __shfl_xor(s, 16, kWave);
+  s += __shfl_xor(s, 32, kWave);
+  const int64_t v = g * 16 + (lane & 15) - shift;
+  if (lane < 16 && v >= 0 && v < V) out[v] = sqrt(s);
+}
+
 // One block: out[0] = max(x[0 .. n)) of non-negative values (0 if n == 0).
 __global__ __launch_bounds__(256) void max_reduce_kernel(const double* __restrict__ x, int32_t n,
                                                          double* __restrict__ out) {
@@ -154,6 +185,14 @@ hipError_t launch_row_norms(const __bf16* X, int32_t n, int32_t D, double* out,
                             hipStream_t stream) {
   if (n <= 0) return hipSuccess;
   row_norms_kernel<<<dim3((n + 3) / 4), 256, 0, stream>>>(X, n, D, out);
+  return hipGetLastError();
+}
+
+hipError_t launch_packed_row_norms(const __bf16* Wp, int32_t V, int32_t D, int32_t vocab_offset,
+                                   double* out, hipStream_t stream) {
+  const int64_t groups = packed_groups(V, vocab_offset);
+  packed_row_norms_kernel<<<dim3(static_cast<unsigned>((groups + 3) / 4)), 256, 0, stream>>>(
+      Wp, V, D, vocab_offset & 3, groups, out);
   return hipGetLastError();
 }
 

@@ -272,3 +272,15 @@ def test_partial_lse_packed_argument_errors(L):
     assert call(pl=None) == bd.FS_ERR_INVALID_ARG
     assert call(wsb=16) == bd.FS_ERR_WORKSPACE
     assert call(B=0, h=None, W=None, T=None, pv=None, pi=None, pl=None, ws=None) == bd.FS_OK
+
+
+def test_online_bounds_packed_argument_errors(L):
+    c = _cuts(0, 512, 1000)
+    assert L.fs_online_bounds_packed(ALIGNED, 1000, 264, 0, c, 2, ALIGNED, WS_ALIGNED, 1 << 30,
+                                     None) == bd.FS_ERR_INVALID_ARG      # D % 32
+    assert L.fs_online_bounds_packed(None, 1000, 256, 0, c, 2, ALIGNED, WS_ALIGNED, 1 << 30,
+                                     None) == bd.FS_ERR_INVALID_ARG
+    assert L.fs_online_bounds_packed(ALIGNED, 1000, 256, -1, c, 2, ALIGNED, WS_ALIGNED, 1 << 30,
+                                     None) == bd.FS_ERR_INVALID_ARG      # negative offset
+    assert L.fs_online_bounds_packed(ALIGNED, 1000, 256, 0, c, 2, ALIGNED, WS_ALIGNED, 8,
+                                     None) == bd.FS_ERR_WORKSPACE

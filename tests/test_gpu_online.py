@@ -287,8 +287,9 @@ def test_packed_aligned_rows_stop_early(norm, B, off):
 @pytest.mark.parametrize("B", [32, 256])
 def test_packed_full_size_confident_and_random(B):
     """Llama-3-8B-shaped head in 8 chunks of 16032 rows (multiples of 16) on
-    fragment-order W: confident weights stop after the first chunk, random
-    weights use all 8; sampled rows against the oracle."""
+    fragment-order W, bounds computed from the packed copy: confident weights
+    stop after the first chunk, random weights use all 8; sampled rows against
+    the oracle."""
     w = wl.LLAMA3_8B
     h = wl.make_h(w, B, DEV)
     T = wl.make_temperature(w, B, DEV)
@@ -299,8 +300,8 @@ def test_packed_full_size_confident_and_random(B):
         W = (wl.make_confident_w(w, h, chunk_rows=w.V // 8, later_std=0.002, device=DEV)
              if kind == "confident" else wl.make_w(w, DEV))
         seed, step = w.sampler_seed(4)
-        later = fsl.online_bounds(W, cuts)
         Wp = fsl.pack_weights(W)
+        later = fsl.online_bounds(Wp, cuts, V=w.V, D=w.D)  # from the packed copy alone
         ids, val, used = fsl.sample_online(h, Wp, T, seed, step, cuts, later, V=w.V)
         torch.cuda.synchronize()
         del Wp
@@ -331,3 +332,23 @@ def test_poisoned_workspace():
         for a, b in zip(got, ref):
             assert torch.equal(a, b)
         assert (ref[2] == 1).any() and (ref[2] > 1).any()
+
+
+@pytest.mark.parametrize("off", [0, 3, 6])
+def test_packed_bounds_match_row_major_and_oracle(off):
+    """fs_online_bounds_packed (row norms read from fragment-order W, padding
+    rows skipped) against the row-major bounds and the oracle's suffix norms."""
+    g = torch.Generator().manual_seed(8 + off)
+    V, D = 1531, 256
+    W = (0.05 * torch.randn(V, D, generator=g)).to(torch.bfloat16)
+    W[700:710] *= 3
+    cuts = np.array([0, 16, 496, 704, 1200, V])
+    Wd = W.to(DEV)
+    rm = to_host(fsl.online_bounds(Wd, cuts))
+    pk = to_host(fsl.online_bounds(fsl.pack_weights(Wd, off), cuts, V=V, D=D, vocab_offset=off))
+    Wb = wl.bf16_bits(W)
+    for c in range(len(cuts) - 1):
+        ref = oracle.max_row_norm(Wb[cuts[c + 1]:]) if cuts[c + 1] < V else 0.0
+        assert pk[c] == pytest.approx(ref, rel=1e-12, abs=0.0), c
+        assert pk[c] == pytest.approx(rm[c], rel=1e-12, abs=0.0), c
+    assert pk[-1] == 0.0
