@@ -284,3 +284,24 @@ def test_online_bounds_packed_argument_errors(L):
                                      None) == bd.FS_ERR_INVALID_ARG      # negative offset
     assert L.fs_online_bounds_packed(ALIGNED, 1000, 256, 0, c, 2, ALIGNED, WS_ALIGNED, 8,
                                      None) == bd.FS_ERR_WORKSPACE
+
+
+def test_selected_config_packed(L):
+    """The packed choice is a valid configuration that reads packed W wherever
+    one applies (host-side logic only; without a device the CU count is
+    unknown and the DMA grids count as unfilled)."""
+    n = L.fs_num_configs()
+    assert L.fs_selected_config_packed(4, 7, 1000) == -1          # invalid D
+    for B, D, V in [(1, 4096, 128256), (32, 4096, 128256), (4, 256, 1000), (1, 5120, 151936),
+                    (64, 8192, 16032), (300, 4096, 128256)]:
+        cp, cr = L.fs_selected_config_packed(B, D, V), L.fs_selected_config(B, D, V)
+        assert 0 <= cp < n and 0 <= cr < n
+        name = L.fs_config_name(cp).decode()
+        assert not name.startswith("ksplit"), name                # K-split reads row-major W only
+        if name.startswith("persist"):
+            assert name.endswith("_ntl1"), name                   # packed persistent twins
+    # the persistent choices at the Llama-3 head
+    assert L.fs_config_name(L.fs_selected_config_packed(1, 4096, 128256)) == \
+        b"persist_nt1_nw16_ks8_p4_ntl1"
+    assert L.fs_config_name(L.fs_selected_config_packed(32, 4096, 128256)) == \
+        b"persist_nt2_nw8_ks16_p4_ntl1"
