@@ -13,8 +13,8 @@ abstract): score s = z / T + g with z = h . W_v and g standard Gumbel noise,
 then one argmax per row over the whole vocabulary; a temperature that is not
 positive means greedy (s = z).  The noise for (seed, step, row, global id gv)
 is word gv mod 4 of Philox-4x32-10 at counter (gv / 4, row, step_lo,
-step_hi) and key (seed_lo, seed_hi), mapped to u = (2 (x >> 9) + 1) 2^-24
-and g = -log(-log u).
+step_hi) and key (seed_lo, seed_hi), mapped to u = (x + 1/2) 2^-32 (all 32
+bits of the word) and g = -log(-log u).
 """
 import ctypes
 import os
@@ -39,7 +39,7 @@ def _load():
                                           ctypes.c_uint32, ctypes.c_uint32]
         lib.oracle_noise_bits.restype = ctypes.c_uint32
         lib.oracle_uniform.argtypes = [ctypes.c_uint32]
-        lib.oracle_uniform.restype = ctypes.c_float
+        lib.oracle_uniform.restype = ctypes.c_double
         lib.oracle_gumbel.argtypes = [ctypes.c_uint32]
         lib.oracle_gumbel.restype = ctypes.c_float
         lib.oracle_logit.argtypes = [ctypes.c_void_p, ctypes.c_void_p, ctypes.c_int32]
@@ -147,8 +147,9 @@ def noise_bits_range(seed, step, row, gv0, n):
 
 
 def uniform_array(bits):
+    """u = (x + 1/2) 2^-32 per word, fp64 (exact)."""
     bits = _c(bits, np.uint32)
-    out = np.empty(bits.shape, np.float32)
+    out = np.empty(bits.shape, np.float64)
     _load().oracle_uniform_array(_ptr(bits), bits.size, _ptr(out))
     return out
 
@@ -312,7 +313,7 @@ def merge_lse(val, ids, lse, T, seed, step):
 # (chunked) sampler with early finalisation".
 # ---------------------------------------------------------------------------
 def gumbel_max():
-    """Largest value of the Gumbel map on the uniform grid, -log(-log(1 - 2^-24))."""
+    """Largest value of the Gumbel map (top word), -log(-log(1 - 2^-33))."""
     return float(_load().oracle_gumbel_max())
 
 

@@ -97,19 +97,22 @@ ORACLE_EXPORT uint32_t oracle_noise_bits(uint64_t seed, uint64_t step,
   return out[gv & 3u];
 }
 
-/* Uniform in the open interval (0,1): the top 23 bits k of the word give the
- * odd multiple (2k+1) * 2^-24.  Exact in fp32; never 0 or 1, so the Gumbel
- * value below is always finite.                                            */
-ORACLE_EXPORT float oracle_uniform(uint32_t bits) {
-  uint32_t k = bits >> 9;
-  double u = (double)(2u * k + 1u) * 0x1p-24;
-  return (float)u; /* exact: 2k+1 < 2^24 */
+/* Uniform in the open interval (0,1): the midpoint of the word's cell of
+ * width 2^-32, u = (x + 1/2) * 2^-32.  All 32 bits of the word count, so two
+ * ids share a noise value only when their words are equal (probability
+ * 2^-32 per pair): with equal logits the largest score is then tied with
+ * probability about V * 2^-33, and the sampler stays exact up to that
+ * granularity (wiki summary, "Key claims": the samples follow the
+ * categorical distribution with no approximation).  Exact in fp64 (33
+ * significant bits); never 0 or 1, so the Gumbel value below is finite.    */
+ORACLE_EXPORT double oracle_uniform(uint32_t bits) {
+  return ((double)bits + 0.5) * 0x1p-32;
 }
 
 /* Standard Gumbel draw by inversion of its CDF exp(-exp(-g)):
  * g = -log(-log u), evaluated in fp64 and rounded once to fp32.            */
 ORACLE_EXPORT float oracle_gumbel(uint32_t bits) {
-  double u = (double)oracle_uniform(bits);
+  double u = oracle_uniform(bits);
   double g = -log(-log(u));
   return (float)g;
 }
@@ -123,7 +126,7 @@ ORACLE_EXPORT void oracle_noise_bits_range(uint64_t seed, uint64_t step,
     out[i] = oracle_noise_bits(seed, step, row, gv0 + (uint32_t)i);
 }
 
-ORACLE_EXPORT void oracle_uniform_array(const uint32_t* bits, int64_t n, float* out) {
+ORACLE_EXPORT void oracle_uniform_array(const uint32_t* bits, int64_t n, double* out) {
 #pragma omp parallel for schedule(static)
   for (int64_t i = 0; i < n; ++i) out[i] = oracle_uniform(bits[i]);
 }
@@ -439,8 +442,8 @@ ORACLE_EXPORT void oracle_lse_logits(const float* z, int32_t V, const float* T, 
  * no bound; the reading built here:
  *   - a later logit obeys z = h . W_v <= |h| * R, R the largest row norm of
  *     the later chunks (Cauchy-Schwarz);
- *   - a noise value is at most g_max, the largest value of the Gumbel map on
- *     the uniform grid, -log(-log(1 - 2^-24));
+ *   - a noise value is at most g_max, the largest value of the Gumbel map,
+ *     taken at the top word: -log(-log(1 - 2^-33));
  *   - row b is final after chunk c when its running best exceeds
  *     (|h_b| * R_c * (1/T) + g_max) * (1 + 2^-8) (greedy rows: |h_b| * R_c *
  *     (1 + 2^-8), no scaling and no noise).  The factor 1 + 2^-8 is a safety
@@ -448,7 +451,7 @@ ORACLE_EXPORT void oracle_lse_logits(const float* z, int32_t V, const float* T, 
  * The samples are those of oracle_sample over the whole vocabulary, whatever
  * the chunks; this function also reports, per row, how many chunks were
  * needed.                                                                  */
-ORACLE_EXPORT double oracle_gumbel_max(void) { return -log(-log(1.0 - ldexp(1.0, -24))); }
+ORACLE_EXPORT double oracle_gumbel_max(void) { return -log(-log(1.0 - ldexp(1.0, -33))); }
 
 /* Euclidean norm of a bf16 row, fp64.                                      */
 static double row_norm(const uint16_t* x, int32_t D) {

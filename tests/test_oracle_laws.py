@@ -65,8 +65,8 @@ def test_greedy_rows_are_library_argmax(orc):
 
 
 def test_small_temperature_limit_is_greedy(orc):
-    """With g bounded on the grid ([-2.81, 16.64]), any 0 < T < gap / 19.45
-    yields the greedy id; T = gap / 40 is well inside."""
+    """With g bounded ([-3.131, 22.874] over all 2^32 words), any
+    0 < T < gap / 26.01 yields the greedy id; T = gap / 40 is well inside."""
     B, D, V = 8, 64, 2000
     hb, Wb = _rand_bf16((B, D), 1.0, 3), _rand_bf16((V, D), 0.1, 4)
     z = _f64(hb) @ _f64(Wb).T

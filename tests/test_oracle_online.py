@@ -118,6 +118,6 @@ def test_max_row_norm_matches_numpy():
 
 
 def test_gumbel_max_closed_form():
-    assert oracle.gumbel_max() == pytest.approx(-np.log(-np.log1p(-2.0 ** -24)), rel=1e-12)
-    # and it is the map's value at the top grid point
+    assert oracle.gumbel_max() == pytest.approx(-np.log(-np.log1p(-2.0 ** -33)), rel=1e-12)
+    # and it is the map's value at the top word
     assert np.float32(oracle.gumbel_max()) == np.float32(oracle.gumbel(0xFFFFFFFF))

@@ -63,7 +63,7 @@ def test_noise_bit_frequencies(orc):
     bits = ((x[:, None] >> np.arange(32, dtype=np.uint32)) & 1).astype(np.float64)
     freq = bits.mean(axis=0)
     assert np.all(np.abs(freq - 0.5) < 4 * 0.5 / np.sqrt(n))
-    u = (x >> 9).astype(np.float64)
+    u = x.astype(np.float64)
     u = (u - u.mean()) / u.std()
     corr = np.mean(u[:-1] * u[1:])
     assert abs(corr) < 5 / np.sqrt(n)
