@@ -16,8 +16,10 @@
  * vocabulary id gv = vocab_offset + v:
  *   x = word (gv mod 4) of Philox4x32_10(counter = {gv / 4, b, step_lo,
  *       step_hi}, key = {seed_lo, seed_hi})
- *   u = (2 (x >> 9) + 1) * 2^-24            (exact fp32, 0 < u < 1)
+ *   u = (x + 1/2) * 2^-32                   (all 32 bits; 0 < u < 1)
  *   g = -log(-log u)
+ * Equal logits therefore tie for the largest score only when two ids draw
+ * the same word (about V * 2^-33 of draws).
  * Keying on the global id makes the field independent of tiling and of
  * vocabulary sharding, so per-shard results merge to the unsharded result
  * (wiki summary, "Method", tensor-parallel paragraph).
@@ -44,7 +46,14 @@
  *     fs_last_error() (thread-local).  Device-resident values are not
  *     inspected: NaN or infinite entries in h or W give undefined ids.
  *   - B == 0 is a no-op that returns FS_OK (pointers may then be NULL).
+ *     The samplers take at most 1048560 (16 * 65535) batch rows per call and
+ *     the unfused baseline at most 65535 (the launch grids' row limit);
+ *     larger B is FS_ERR_UNSUPPORTED.
  *   - Reentrant: concurrent calls are safe if they use distinct workspaces.
+ *   - Failure testing: with FS_FAULT_INJECT=launch in the environment, every
+ *     entry point that would launch device work returns FS_ERR_HIP once its
+ *     arguments have passed the checks, and launches nothing;
+ *     fs_last_error() then names the injection.
  */
 #ifndef FLASHSAMPLE_H
 #define FLASHSAMPLE_H
@@ -202,7 +211,7 @@ FS_API fs_status fs_merge_lse(const float* partial_val, const int32_t* partial_i
  *     (|h_b| * later_norm[c] * fp32(1/T_b) + g_max) * (1 + 2^-8)
  * (greedy rows: |h_b| * later_norm[c] * (1 + 2^-8)), where later_norm[c] is
  * the largest row norm of W over the chunks after c and g_max =
- * -log(-log(1 - 2^-24)) the largest Gumbel value of the noise field.  No later
+ * -log(-log(1 - 2^-33)) the largest Gumbel value of the noise field.  No later
  * score can overtake such a row, so the ids and scores are those of
  * fs_sample over the whole of W; only the work changes.  Once every row is
  * final the remaining chunks' kernels return without reading their W rows.

@@ -39,6 +39,32 @@ fs_status hip_fail(hipError_t e, const char* what) {
 
 bool aligned(const void* p, size_t a) { return (reinterpret_cast<uintptr_t>(p) % a) == 0; }
 
+// Testing hook for failure handling: with FS_FAULT_INJECT=launch in the
+// environment, every entry point that would launch device work returns
+// FS_ERR_HIP once its arguments have passed the checks, before its first
+// launch, with the reason in fs_last_error(): the path a failed launch
+// takes, without a device and without launching anything.
+bool launch_fault_injected() {
+  const char* f = getenv("FS_FAULT_INJECT");
+  return f != nullptr && std::strcmp(f, "launch") == 0;
+}
+
+fs_status injected_failure(const char* who) {
+  return fail(FS_ERR_HIP, "%s: launch failure injected (FS_FAULT_INJECT=launch)", who);
+}
+
+// Name of a configuration for messages (never a null pointer).
+const char* config_label(int cfg) {
+  const char* n = fs::fused_config_name(cfg);
+  return n != nullptr ? n : "(none)";
+}
+
+// Largest batch the batch-tiled kernels can take: their batch blocks (16 or
+// more rows each) form the grid's y dimension, at most 65535 blocks.
+constexpr int32_t kMaxFusedB = 16 * 65535;
+// The unfused baseline's row kernels put one batch row per grid row.
+constexpr int32_t kMaxUnfusedB = 65535;
+
 constexpr int64_t kMaxId = 2147483647;  // ids are int32
 
 fs_status check_shape(int32_t B, int32_t D, int32_t V, int32_t vocab_offset) {
@@ -119,13 +145,17 @@ fs_status run_fused(const void* h, const void* W, int32_t B, int32_t D, int32_t 
                 workspace_bytes, need);
   if (w_packed && D % 32 != 0)
     return fail(FS_ERR_INVALID_ARG, "%s: D must be a multiple of 32 (got %d)", who, D);
+  if (B > kMaxFusedB)
+    return fail(FS_ERR_UNSUPPORTED, "%s: B=%d exceeds the %d batch rows one call can take", who,
+                B, kMaxFusedB);
   const int cfg = choose_config(B, D, V, w_packed);
   if (!fs::fused_config_supports(cfg, B, D))
     return fail(FS_ERR_UNSUPPORTED, "%s: forced configuration %s does not support B=%d, D=%d",
-                who, fs::fused_config_name(cfg), B, D);
+                who, config_label(cfg), B, D);
   if (w_packed && !fs::fused_config_reads_packed(cfg))
     return fail(FS_ERR_UNSUPPORTED, "%s: configuration %s for B=%d, D=%d, V=%d has no packed-W kernel",
-                who, fs::fused_config_name(cfg), B, D, V);
+                who, config_label(cfg), B, D, V);
+  if (launch_fault_injected()) return injected_failure(who);
   const size_t S = max_splits(V);
   fs::SampleArgs a;
   a.h = static_cast<const __bf16*>(h);
@@ -169,7 +199,7 @@ fs_status run_fused(const void* h, const void* W, int32_t B, int32_t D, int32_t 
   if (e != hipSuccess) return hip_fail(e, "merge launch");
   if (getenv("FS_LOG"))
     fprintf(stderr, "[flashsample] %s B=%d D=%d V=%d config=%s splits=%d\n", who, B, D, V,
-            fs::fused_config_name(cfg), a.S);
+            config_label(cfg), a.S);
   return FS_OK;
 }
 
@@ -232,6 +262,9 @@ static fs_status run_online(const void* h, const void* W, int32_t B, int32_t D, 
   if (D > kMaxOnlineD)
     return fail(FS_ERR_UNSUPPORTED, "%s: D=%d exceeds %d, where the bound's rounding margin holds",
                 who, D, kMaxOnlineD);
+  if (B > kMaxFusedB)
+    return fail(FS_ERR_UNSUPPORTED, "%s: B=%d exceeds the %d batch rows one call can take", who,
+                B, kMaxFusedB);
   const size_t need = online_workspace(B, V, n_chunks);
   if (workspace_bytes < need)
     return fail(FS_ERR_WORKSPACE, "%s: workspace of %zu bytes is below the %zu required", who,
@@ -241,11 +274,12 @@ static fs_status run_online(const void* h, const void* W, int32_t B, int32_t D, 
     const int cfg = choose_config(B, D, cuts[c + 1] - cuts[c], packed);
     if (!fs::fused_config_supports(cfg, B, D))
       return fail(FS_ERR_UNSUPPORTED, "%s: forced configuration %s does not support B=%d, D=%d",
-                  who, fs::fused_config_name(cfg), B, D);
+                  who, config_label(cfg), B, D);
     if (packed && !fs::fused_config_reads_packed(cfg))
       return fail(FS_ERR_UNSUPPORTED, "%s: configuration %s has no packed-W kernel", who,
-                  fs::fused_config_name(cfg));
+                  config_label(cfg));
   }
+  if (launch_fault_injected()) return injected_failure(who);
   const size_t S = max_splits(V);
   const size_t region = fs::round_up(sizeof(float) * B * S, 256);
   char* ws = static_cast<char*>(workspace);
@@ -257,8 +291,8 @@ static fs_status run_online(const void* h, const void* W, int32_t B, int32_t D, 
   int32_t* done = reinterpret_cast<int32_t*>(tail);
   tail += fs::round_up(sizeof(int32_t) * B, 256);
   int32_t* live = reinterpret_cast<int32_t*>(tail);
-  // largest value of the Gumbel map on the uniform grid: u = 1 - 2^-24
-  const double g_max = -std::log(-std::log1p(-0x1p-24));
+  // largest value of the Gumbel map, at the top word: u = 1 - 2^-33
+  const double g_max = -std::log(-std::log1p(-0x1p-33));
   const double margin = 1.0 + 0x1p-8;
   const hipStream_t st = static_cast<hipStream_t>(stream);
   hipError_t e = fs::launch_online_init(static_cast<const __bf16*>(h), B, D, n_chunks, hnorm,
@@ -310,6 +344,7 @@ static fs_status run_online_bounds(const void* W, int32_t V, int32_t D, int32_t 
   if (workspace_bytes < need)
     return fail(FS_ERR_WORKSPACE, "fs_online_bounds: workspace of %zu bytes is below the %zu required",
                 workspace_bytes, need);
+  if (launch_fault_injected()) return injected_failure("fs_online_bounds");
   const hipStream_t st = static_cast<hipStream_t>(stream);
   double* norms = static_cast<double*>(workspace);
   double* chunk_max = reinterpret_cast<double*>(static_cast<char*>(workspace) +
@@ -367,6 +402,7 @@ fs_status fs_pack_weights(const void* W, int32_t V, int32_t D, int32_t vocab_off
   if (packed_bytes < need)
     return fail(FS_ERR_WORKSPACE, "fs_pack_weights: %zu bytes for W_packed, %zu required",
                 packed_bytes, need);
+  if (launch_fault_injected()) return injected_failure("fs_pack_weights");
   hipError_t e = fs::launch_pack_weights(static_cast<const __bf16*>(W), V, D, vocab_offset,
                                          static_cast<__bf16*>(W_packed),
                                          static_cast<hipStream_t>(stream));
@@ -429,6 +465,7 @@ fs_status fs_merge_lse(const float* partial_val, const int32_t* partial_idx,
     return fail(FS_ERR_INVALID_ARG, "pointers must be 4-byte aligned");
   if (static_cast<int64_t>(P) * B > (int64_t{1} << 40))
     return fail(FS_ERR_INVALID_ARG, "P * B too large");
+  if (launch_fault_injected()) return injected_failure("fs_merge_lse");
   hipError_t e = fs::launch_merge_groups_lse(partial_val, partial_idx, partial_lse, P, B,
                                              temperature, seed, step, out_ids, out_maxval,
                                              out_lse, static_cast<hipStream_t>(stream));
@@ -495,6 +532,7 @@ fs_status fs_merge(const float* partial_val, const int32_t* partial_idx, int32_t
     return fail(FS_ERR_INVALID_ARG, "pointers must be 4-byte aligned");
   if (static_cast<int64_t>(P) * B > (int64_t{1} << 40))
     return fail(FS_ERR_INVALID_ARG, "P * B too large");
+  if (launch_fault_injected()) return injected_failure("fs_merge");
   hipError_t e = fs::launch_merge(partial_val, partial_idx, P, B, B, 1, out_ids, out_maxval,
                                   static_cast<hipStream_t>(stream));
   if (e != hipSuccess) return hip_fail(e, "merge launch");
@@ -508,10 +546,14 @@ fs_status fs_sample_unfused(const void* h, const void* W, int32_t B, int32_t D, 
   fs_status s = check_sample_args(h, W, B, D, V, vocab_offset, temperature, out_ids,
                                   out_maxval, workspace);
   if (s != FS_OK || B == 0) return s;
+  if (B > kMaxUnfusedB)
+    return fail(FS_ERR_UNSUPPORTED, "fs_sample_unfused: B=%d exceeds the %d batch rows one call can take",
+                B, kMaxUnfusedB);
   const size_t need = fs::unfused_workspace_bytes(B, V);
   if (workspace_bytes < need)
     return fail(FS_ERR_WORKSPACE, "fs_sample_unfused: workspace of %zu bytes is below the %zu required",
                 workspace_bytes, need);
+  if (launch_fault_injected()) return injected_failure("fs_sample_unfused");
   fs::SampleArgs a;
   a.h = static_cast<const __bf16*>(h);
   a.W = static_cast<const __bf16*>(W);
@@ -540,6 +582,7 @@ fs_status fs_debug_noise(uint64_t seed, uint64_t step, uint32_t row, uint32_t gv
   if (n == 0 || (!out_bits && !out_gumbel)) return FS_OK;
   if ((out_bits && !aligned(out_bits, 4)) || (out_gumbel && !aligned(out_gumbel, 4)))
     return fail(FS_ERR_INVALID_ARG, "outputs must be 4-byte aligned");
+  if (launch_fault_injected()) return injected_failure("fs_debug_noise");
   hipError_t e = fs::launch_debug_noise(seed, step, row, gv0, n, out_bits, out_gumbel,
                                         static_cast<hipStream_t>(stream));
   if (e != hipSuccess) return hip_fail(e, "noise launch");
@@ -552,6 +595,7 @@ fs_status fs_debug_gumbel(const uint32_t* bits, int64_t n, float* out_gumbel, vo
   if (!bits || !out_gumbel) return fail(FS_ERR_INVALID_ARG, "null pointer argument");
   if (!aligned(bits, 4) || !aligned(out_gumbel, 4))
     return fail(FS_ERR_INVALID_ARG, "pointers must be 4-byte aligned");
+  if (launch_fault_injected()) return injected_failure("fs_debug_gumbel");
   hipError_t e = fs::launch_debug_gumbel(bits, n, out_gumbel, static_cast<hipStream_t>(stream));
   if (e != hipSuccess) return hip_fail(e, "gumbel launch");
   return FS_OK;

@@ -79,35 +79,35 @@ __device__ __forceinline__ uint32_t pick_word(u32x4 w, uint32_t i) {
   return i == 0 ? w.x : i == 1 ? w.y : i == 2 ? w.z : w.w;
 }
 
-// Standard Gumbel value of a 32-bit word: u = (2k+1) 2^-24 with k the top 23
-// bits, g = -ln(-ln u).
+// Standard Gumbel value of a 32-bit word x: u = (x + 1/2) 2^-32, the midpoint
+// of the word's cell (all 32 bits count), and g = -ln(-ln u).
 //
 // Cost matters: this runs once per logit of the B x V tile, so it uses the
 // hardware base-2 logarithm (v_log_f32) instead of the library's
-// extended-precision logf/log1pf (about ten times the instructions).  The one
-// place the hardware log is not accurate enough is -ln u for u near 1, where
+// extended-precision logf/log1pf (about ten times the instructions).  The
+// one place where that is not accurate enough is -ln u for u near 1, where
 // the winners of a large vocabulary sit (u ~ 1 - 1/V): there ln u is a small
-// difference and an absolute error in log2 becomes a large relative error in
-// -ln u, which the outer log turns into an absolute error in g.  Both u and
-// v = 1 - u = (2^24 - 1 - 2k) 2^-24 are exact in fp32, so for v <= 1/16 the
-// series -ln(1 - v) = v + v^2/2 + ... + v^5/5 (truncation below 1.6e-7
-// relative) is used instead.  Elsewhere |ln u| >= 0.06 and the hardware log
-// is used directly.  The device values are checked against the fp64 oracle
-// on all 2^23 grid points.
+// difference and an absolute error in log2 u becomes a large relative error
+// in -ln u, which the outer log turns into an absolute error in g.  So both
+// u and v = 1 - u are formed from the word itself, v from its complement:
+// v = (~x + 1/2) 2^-32.  Each is one conversion and one fused multiply-add,
+// within 2^-23 relative of the exact value (exact for ~x < 2^23, where the
+// largest scores of a big vocabulary come from).  For v <= 1/16 the series
+// -ln(1 - v) = v + v^2/2 + ... + v^5/5 (truncation below 1.6e-7 relative)
+// gives -ln u; elsewhere |ln u| >= 0.06 and the hardware log of u is used.
+// Checked against the fp64 oracle on the top 2^24 and bottom 2^20 words and
+// on a stratified grid of the rest.
 __device__ __forceinline__ float gumbel_from_bits(uint32_t x) {
   constexpr float kLn2 = 0.693147180559945309f;
-  const float u = static_cast<float>(2u * (x >> 9) + 1u) * 0x1p-24f;  // exact
-  // v = 1 - u is exact for u >= 1/2 (Sterbenz), so wherever the series below
-  // is used; the series stops at v^5/5, a relative truncation error below
-  // v^5/6 <= 1.6e-7 for v <= 1/16.
-  const float v = 1.0f - u;
+  const float u = __builtin_fmaf(static_cast<float>(x), 0x1p-32f, 0x1p-33f);
+  const float v = __builtin_fmaf(static_cast<float>(~x), 0x1p-32f, 0x1p-33f);
   float series = 1.0f / 5.0f;
   series = __builtin_fmaf(series, v, 1.0f / 4.0f);
   series = __builtin_fmaf(series, v, 1.0f / 3.0f);
   series = __builtin_fmaf(series, v, 1.0f / 2.0f);
   series = __builtin_fmaf(series, v, 1.0f);
   series *= v;
-  const float neg_ln_u = u >= 0.9375f ? series : -__builtin_amdgcn_logf(u) * kLn2;
+  const float neg_ln_u = v <= 0.0625f ? series : -__builtin_amdgcn_logf(u) * kLn2;
   return -__builtin_amdgcn_logf(neg_ln_u) * kLn2;
 }
 

@@ -10,7 +10,7 @@
 // The pages give no stopping bound; this one follows from Cauchy-Schwarz.  A
 // later logit obeys z = h_b . W_v <= |h_b| R_c, with R_c the largest row norm
 // of the chunks after c, and a noise value is at most g_max, the largest
-// value of the Gumbel map on the uniform grid.  Row b is therefore final
+// value of the Gumbel map (at the top word).  Row b is therefore final
 // after chunk c when its running best exceeds
 //     (|h_b| R_c (1/T) + g_max) (1 + 2^-8)      (greedy rows: |h_b| R_c (1 + 2^-8)).
 // The factor 1 + 2^-8 covers the rounding of the device's fp32 logits (at

@@ -370,7 +370,11 @@ hipError_t launch_cfg(SampleArgs& a, hipStream_t stream) {
   }
   a.S = (a.V + (a.vocab_offset & 3) + rows - 1) / rows;
   const int nb = batch_blocks<Loop>(a.B);
-  const dim3 grid = is_xcd_paired<Loop>::value ? dim3((a.S + kXcds - 1) / kXcds * kXcds * nb)
+  // grid limits: x < 2^31 blocks, y <= 65535 (checked here, before launching)
+  const int64_t paired_x = static_cast<int64_t>((a.S + kXcds - 1) / kXcds) * kXcds * nb;
+  if (nb > 65535 || (is_xcd_paired<Loop>::value && paired_x > 0x7FFFFFFF))
+    return hipErrorInvalidConfiguration;
+  const dim3 grid = is_xcd_paired<Loop>::value ? dim3(static_cast<unsigned>(paired_x))
                                                : dim3(a.S, nb);
   const dim3 block(Loop::NW * kWave);
   if (a.w_packed) {

@@ -152,7 +152,7 @@ __global__ __launch_bounds__(kThreads) void softmax_stats_kernel(const float* z,
   float l = 0.f;
   for (int v = v_begin + threadIdx.x; v < v_end; v += kThreads) l += expf(zr[v] * inv_t - m);
   l = block_sum(l, sh);
-  if (threadIdx.x == 0) stats[b * C + c] = make_float2(m, l);
+  if (threadIdx.x == 0) stats[static_cast<int64_t>(b) * C + c] = make_float2(m, l);
 }
 
 // grid (C, B): p = exp(z / T - lse), lse combined from the chunk statistics.
@@ -165,11 +165,11 @@ __global__ __launch_bounds__(kThreads) void softmax_probs_kernel(
   if (row_is_greedy(T)) return;
   const float inv_t = row_inv_temperature(T);
   float m = -__builtin_inff();
-  for (int i = threadIdx.x; i < C; i += kThreads) m = fmaxf(m, stats[b * C + i].x);
+  for (int i = threadIdx.x; i < C; i += kThreads) m = fmaxf(m, stats[static_cast<int64_t>(b) * C + i].x);
   m = block_max(m, sh);
   float l = 0.f;
   for (int i = threadIdx.x; i < C; i += kThreads) {
-    const float2 st = stats[b * C + i];
+    const float2 st = stats[static_cast<int64_t>(b) * C + i];
     l += st.y * expf(st.x - m);
   }
   l = block_sum(l, sh);
@@ -220,8 +220,8 @@ __global__ __launch_bounds__(kThreads) void gumbel_argmax_kernel(
     r.init();
 #pragma unroll
     for (int w = 0; w < kThreads / kWave; ++w) r.push(s_v[w], s_i[w]);
-    part_val[b * C + c] = r.v;
-    part_idx[b * C + c] = r.i;
+    part_val[static_cast<int64_t>(b) * C + c] = r.v;
+    part_idx[static_cast<int64_t>(b) * C + c] = r.i;
   }
 }
 
@@ -230,8 +230,9 @@ __global__ __launch_bounds__(kThreads) void gumbel_argmax_kernel(
 size_t unfused_workspace_bytes(int32_t B, int32_t V) {
   const size_t ldz = round_up(static_cast<size_t>(V), 64);
   const size_t C = (static_cast<size_t>(V) + kChunk - 1) / kChunk;
-  return round_up(4 * B * ldz, 256) * 2 + round_up(8 * B * C, 256) + round_up(4 * B, 256) +
-         round_up(4 * B * C, 256) * 2;
+  const size_t rows = static_cast<size_t>(B);
+  return round_up(sizeof(float) * rows * ldz, 256) * 2 + round_up(sizeof(double) * rows * C, 256) +
+         round_up(sizeof(float) * rows, 256) + round_up(sizeof(float) * rows * C, 256) * 2;
 }
 
 hipError_t launch_unfused(const SampleArgs& a, int32_t* out_ids, float* out_val,

@@ -1,10 +1,12 @@
 """The C-ABI library loads, exports what include/flashsample.h declares, and
 rejects bad arguments on the host before any HIP call (CPU only: no call in
-this file reaches a kernel launch)."""
+this file launches a kernel -- the calls with valid arguments run under
+FS_FAULT_INJECT=launch, or only where no GPU is present)."""
 import ctypes
 
 import pytest
 
+from conftest import gpu_available
 from lm_head_exact_amd import binding as bd
 
 ALIGNED = 0x10000            # fake, never dereferenced: every call below fails validation
@@ -62,7 +64,8 @@ def test_argument_errors(L, fn, kw, status):
 
 
 def test_workspace_sizes(L):
-    assert L.fs_workspace_bytes(0, 256, 1000) == 0 or L.fs_workspace_bytes(0, 256, 1000) >= 0
+    # B = 0 is a valid no-op and needs no workspace
+    assert L.fs_workspace_bytes(0, 256, 1000) == 0
     assert L.fs_workspace_bytes(4, 7, 1000) == 0          # invalid D
     ws = L.fs_workspace_bytes(32, 4096, 128256)
     assert ws >= 8 * 32 * (128256 // 64) and ws % 256 == 0
@@ -305,3 +308,70 @@ def test_selected_config_packed(L):
         b"persist_nt1_nw16_ks8_p4_ntl1"
     assert L.fs_config_name(L.fs_selected_config_packed(32, 4096, 128256)) == \
         b"persist_nt2_nw8_ks16_p4_ntl1"
+
+
+def test_unfused_workspace_size_does_not_wrap(L):
+    """Sizes are computed in size_t: at B = 2^29 the logits alone take
+    4 * B * ldz bytes, past the range of a 32-bit product."""
+    B, V = 1 << 29, 64
+    need = L.fs_unfused_workspace_bytes(B, 8, V)
+    assert need >= 2 * 4 * B * V
+    assert L.fs_unfused_workspace_bytes(2 * B, 8, V) >= 2 * need - 4096
+
+
+def test_batch_limits_are_refused_on_the_host(L):
+    # the unfused baseline puts one batch row per grid row (at most 65535)
+    assert _sample(L, "fs_sample_unfused", B=65536, wsb=1 << 62) == bd.FS_ERR_UNSUPPORTED
+    assert b"65535" in L.fs_last_error()
+    # the samplers' batch blocks (>= 16 rows) form the grid's y dimension
+    for fn in ("fs_sample", "fs_sample_partial", "fs_sample_packed"):
+        assert _sample(L, fn, B=16 * 65535 + 1, wsb=1 << 62) == bd.FS_ERR_UNSUPPORTED, fn
+        assert b"1048560" in L.fs_last_error()
+
+
+@pytest.fixture
+def inject(monkeypatch):
+    monkeypatch.setenv("FS_FAULT_INJECT", "launch")
+    yield
+
+
+def test_injected_launch_failure_every_entry_point(L, inject):
+    """With FS_FAULT_INJECT=launch a call whose arguments pass the checks
+    returns FS_ERR_HIP with the reason in fs_last_error, and launches
+    nothing (the fake pointers below are never touched)."""
+    A, WS, big = ALIGNED, WS_ALIGNED, 1 << 40
+    cuts = (ctypes.c_int32 * 3)(0, 512, 1000)
+    calls = {
+        "fs_sample": lambda: _sample(L, "fs_sample"),
+        "fs_sample_partial": lambda: _sample(L, "fs_sample_partial"),
+        "fs_sample_packed": lambda: _sample(L, "fs_sample_packed"),
+        "fs_sample_unfused": lambda: _sample(L, "fs_sample_unfused"),
+        "fs_sample_partial_lse": lambda: _sample_lse(L),
+        "fs_merge": lambda: L.fs_merge(A, A, 3, 4, A, A, None),
+        "fs_merge_lse": lambda: L.fs_merge_lse(A, A, A, 3, 4, A, 1, 2, A, A, A, None),
+        "fs_pack_weights": lambda: L.fs_pack_weights(A, 1000, 256, 0, A, big, None),
+        "fs_online_bounds": lambda: L.fs_online_bounds(A, 1000, 256, cuts, 2, A, WS, big, None),
+        "fs_sample_online": lambda: L.fs_sample_online(A, A, 4, 256, 1000, 0, A, 1, 2, cuts, 2,
+                                                       A, A, A, A, WS, big, None),
+        "fs_debug_noise": lambda: L.fs_debug_noise(0, 0, 0, 0, 16, A, A, None),
+        "fs_debug_gumbel": lambda: L.fs_debug_gumbel(A, 16, A, None),
+    }
+    for name, call in calls.items():
+        assert call() == bd.FS_ERR_HIP, name
+        msg = L.fs_last_error()
+        assert name.encode() in msg and b"FS_FAULT_INJECT" in msg, (name, msg)
+
+
+def test_injection_does_not_mask_argument_errors(L, inject):
+    assert _sample(L, D=7) == bd.FS_ERR_INVALID_ARG
+    assert _sample(L, wsb=16) == bd.FS_ERR_WORKSPACE
+    assert _sample(L, B=0, h=None, W=None, T=None, ids=None, val=None, ws=None) == bd.FS_OK
+
+
+@pytest.mark.skipif(gpu_available(), reason="needs a machine without a GPU")
+def test_launch_without_a_device_reports_the_runtime_error(L, monkeypatch):
+    """Where no device exists the launch itself fails: FS_ERR_HIP carries
+    the runtime's message."""
+    monkeypatch.delenv("FS_FAULT_INJECT", raising=False)
+    assert _sample(L) == bd.FS_ERR_HIP
+    assert len(L.fs_last_error()) > 0 and b"FS_FAULT_INJECT" not in L.fs_last_error()

@@ -74,7 +74,10 @@ def test_layout_matches_definition(V, D, off):
 def test_every_packed_config_equals_row_major(cfg):
     if not _packed_capable(cfg):
         pytest.skip("configuration without a packed-W kernel")
-    shapes = [(37, 256, 1531, 5), (4, 256, 1000, 0), (300, 128, 700, 2)]
+    # the last three fit the persistent kernels (D = 32 * waves * k-steps,
+    # B <= 16 or 32), at offsets that do and do not start on a Philox block
+    shapes = [(37, 256, 1531, 5), (4, 256, 1000, 0), (300, 128, 700, 2),
+              (29, 4096, 1531, 5), (4, 4096, 1000, 0), (16, 8192, 1000, 6)]
     ran = 0
     fsl.force_config(cfg)
     for B, D, V, off in shapes:
@@ -161,7 +164,8 @@ def test_every_packed_config_partial_lse_equals_row_major(cfg):
         pytest.skip("configuration without a packed-W kernel")
     fsl.force_config(cfg)
     ran = 0
-    for B, D, V, off in [(37, 256, 1531, 6), (4, 256, 1000, 0), (300, 128, 700, 48097)]:
+    for B, D, V, off in [(37, 256, 1531, 6), (4, 256, 1000, 0), (300, 128, 700, 48097),
+                         (29, 4096, 1531, 7), (4, 4096, 1000, 0), (16, 8192, 1000, 6)]:
         h, W, T = _rand(B, D, V, seed=2 * B + V)
         outs = []
         try:
@@ -180,6 +184,8 @@ def test_every_packed_config_partial_lse_equals_row_major(cfg):
         assert np.array_equal(i0, i1), fsl.config_name(cfg)
         assert np.array_equal(v0.view(np.uint32), v1.view(np.uint32)), fsl.config_name(cfg)
         assert np.array_equal(l0.view(np.uint32), l1.view(np.uint32)), fsl.config_name(cfg)
+        check_rows(wl.bf16_bits(h), wl.bf16_bits(W), to_host(T), 7, 2, off, i1, v1,
+                   label=f"packed lse {fsl.config_name(cfg)} B={B} D={D}")
         ran += 1
     if ran == 0:
         pytest.skip("configuration supports none of the test shapes")
