@@ -56,6 +56,8 @@ def parse():
     ap.add_argument("--no-online", action="store_true")
     ap.add_argument("--no-packed", action="store_true")
     ap.add_argument("--profile-pass", action="store_true")
+    ap.add_argument("--profile-workload", default="llama3-8b-lm-head",
+                    help="workload of --profile-pass (a name from lm_head_exact_amd.workloads)")
     return ap.parse_args()
 
 
@@ -131,9 +133,55 @@ def time_steps(torch, fn, steps, warmup, stream):
     return start.elapsed_time(stop) / steps
 
 
+def step_percentiles(torch, fn, steps, warmup, stream):
+    """Each of `steps` calls timed on its own (an event before and after it on
+    `stream`); returns (p10, median, p90) in microseconds."""
+    for i in range(warmup):
+        fn(i)
+    torch.cuda.synchronize()
+    ev = [torch.cuda.Event(enable_timing=True) for _ in range(steps + 1)]
+    ev[0].record(stream)
+    for i in range(steps):
+        fn(warmup + i)
+        ev[i + 1].record(stream)
+    torch.cuda.synchronize()
+    d = sorted(ev[i].elapsed_time(ev[i + 1]) * 1e3 for i in range(steps))
+
+    def q(f):
+        return d[min(len(d) - 1, int(round(f * (len(d) - 1))))]
+    return q(0.10), q(0.50), q(0.90)
+
+
+def device_peaks(fsl, dev):
+    """CU count and peak shader clock the HIP runtime reports (through the
+    library), and the dense bf16 MFMA peak they imply: CUs x 4 SIMDs x one
+    16x16x32 MFMA (8192 multiply-adds) per 16 clocks per SIMD x 2 FLOP x
+    clock.  The roofline uses the published peaks; this is printed beside
+    them."""
+    cus, clock_khz = fsl.device_info(dev.index or 0)
+    peak = cus * 4 * (8192 / 16) * 2 * clock_khz * 1e3 / 1e12
+    return {"cus": cus, "clock_khz": clock_khz,
+            "bf16_dense_tflops_from_clock": round(peak, 1),
+            "bf16_dense_tflops_used": MFMA_BF16_PEAK_TFLOPS, "hbm_gbs_used": HBM_PEAK_GBS}
+
+
+def cpu_model():
+    try:
+        for line in open("/proc/cpuinfo"):
+            if line.startswith("model name"):
+                return line.split(":", 1)[1].strip()
+    except OSError:
+        pass
+    return None
+
+
 def measure_fused_kernel(torch, fsl, fn, steps, warmup):
-    """Average duration of the fused kernel alone (HIP events recorded by the
-    library around each launch on the caller's stream)."""
+    """Launch bracket of the fused kernel: HIP events the library records on
+    the caller's stream right before and right after each fused-kernel launch
+    (fs_profile_enable).  The bracket holds the kernel and its dispatch after
+    the preceding work on the stream, not the tile merge that follows it;
+    rocprofv3's kernel trace gives the kernel alone (a few microseconds
+    less).  Returns (mean, min, max) in ms and the launch count."""
     for i in range(warmup):
         fn(i)
     torch.cuda.synchronize()
@@ -189,7 +237,25 @@ def main():
         return fn, (h, T, out, ws)
 
     if args.profile_pass:
-        fn, keep = make_step(args.batch, packed=Wp is not None)
+        pw = wl.WORKLOADS[args.profile_workload]
+        if pw is wlk:
+            fn, keep = make_step(args.batch, packed=Wp is not None)
+        else:  # another head: its own weights (packed unless --no-packed) and inputs
+            del W, Wp
+            Wx = wl.make_w(pw, dev)
+            Wpx = fsl.pack_weights(Wx, pw.vocab_offset) if not args.no_packed else None
+            hx, Tx = wl.make_h(pw, args.batch, dev), wl.make_temperature(pw, args.batch, dev)
+            outx = (torch.empty(args.batch, dtype=torch.int32, device=dev),
+                    torch.empty(args.batch, dtype=torch.float32, device=dev))
+            wsx = fsl.alloc_workspace(fsl.workspace_bytes(args.batch, pw.D, pw.V), dev)
+
+            def fn(i):
+                seed, step = pw.sampler_seed(i)
+                if Wpx is not None:
+                    fsl.sample_packed(hx, Wpx, pw.V, Tx, seed, step, pw.vocab_offset, out=outx,
+                                      workspace=wsx)
+                else:
+                    fsl.sample(hx, Wx, Tx, seed, step, pw.vocab_offset, out=outx, workspace=wsx)
         for i in range(5):
             fn(i)
         torch.cuda.synchronize()
@@ -197,13 +263,15 @@ def main():
         dst = torch.empty_like(src)
         dst.copy_(src)          # 1 GiB read + 1 GiB write: counter calibration
         torch.cuda.synchronize()
-        print(json.dumps({"profile_pass": True, "B": args.batch, "copy_bytes": 1 << 30}))
+        print(json.dumps({"profile_pass": True, "workload": args.profile_workload, "B": args.batch,
+                          "copy_bytes": 1 << 30}))
         return
 
     B = args.batch
     headline_packed = Wp is not None
     fn, keep = make_step(B, packed=headline_packed)
     ms = time_steps(torch, fn, args.steps, args.warmup, stream)
+    p10, p50, p90 = step_percentiles(torch, fn, max(args.steps, 100), args.warmup, stream)
     k_ms, k_lo, k_hi, k_n = measure_fused_kernel(torch, fsl, fn, args.steps, args.warmup)
     us = ms * 1e3
     k_us = k_ms * 1e3
@@ -214,7 +282,7 @@ def main():
         r_ms = time_steps(torch, rfn, args.steps, args.warmup, stream)
         rk_ms, _, _, _ = measure_fused_kernel(torch, fsl, rfn, args.steps, args.warmup)
         row_major = {"config": fsl.config_name(fsl.selected_config(B, D, V)),
-                     "us_per_step": round(r_ms * 1e3, 2), "kernel_us": round(rk_ms * 1e3, 2),
+                     "us_per_step": round(r_ms * 1e3, 2), "launch_bracket_us": round(rk_ms * 1e3, 2),
                      "frac_of_roofline": round(roofline_us(B, D, V) / (r_ms * 1e3), 4)}
         del rkeep
     bytes_ = algorithmic_bytes(B, D, V)
@@ -223,22 +291,27 @@ def main():
     for b in [int(x) for x in args.sweep.split(",") if x]:
         f, kp = make_step(b)
         t = time_steps(torch, f, args.sweep_steps, 10, stream) * 1e3
+        q10, q50, q90 = step_percentiles(torch, f, args.sweep_steps, 5, stream)
         kt, _, _, _ = measure_fused_kernel(torch, fsl, f, args.sweep_steps, 5)
         kt *= 1e3
         entry = {"B": b, "config": fsl.config_name(fsl.selected_config(b, D, V)),
-                 "us_per_step": round(t, 2), "kernel_us": round(kt, 2),
+                 "us_per_step": round(t, 2),
+                 "us_per_step_p10_p50_p90": [round(q10, 2), round(q50, 2), round(q90, 2)],
+                 "launch_bracket_us": round(kt, 2),
                  "roofline_us": round(roofline_us(b, D, V), 2),
                  "frac_of_roofline": round(roofline_us(b, D, V) / t, 4),
-                 "kernel_hbm_GBs": round(algorithmic_bytes(b, D, V) / (kt * 1e3), 1),
-                 "kernel_mfma_TFLOPs": round(flops(b, D, V) / (kt * 1e6), 1),
+                 "launch_hbm_GBs": round(algorithmic_bytes(b, D, V) / (kt * 1e3), 1),
+                 "launch_mfma_TFLOPs": round(flops(b, D, V) / (kt * 1e6), 1),
                  "tokens_per_s": round(b / (t * 1e-6), 1)}
         if Wp is not None:
             pf, pkp = make_step(b, packed=True)
             pt = time_steps(torch, pf, args.sweep_steps, 10, stream) * 1e3
+            r10, r50, r90 = step_percentiles(torch, pf, args.sweep_steps, 5, stream)
             pkt, _, _, _ = measure_fused_kernel(torch, fsl, pf, args.sweep_steps, 5)
             entry["packed_config"] = fsl.config_name(fsl.selected_config(b, D, V, packed=True))
             entry["packed_us_per_step"] = round(pt, 2)
-            entry["packed_kernel_us"] = round(pkt * 1e3, 2)
+            entry["packed_us_per_step_p10_p50_p90"] = [round(r10, 2), round(r50, 2), round(r90, 2)]
+            entry["packed_launch_bracket_us"] = round(pkt * 1e3, 2)
             entry["packed_frac_of_roofline"] = round(roofline_us(b, D, V) / pt, 4)
             del pkp
         if not args.no_unfused:
@@ -430,11 +503,30 @@ def main():
         oracle.sample(h_cpu[:1], W_cpu, T_cpu[:1], *wlk.sampler_seed(0))
         dt1 = time.perf_counter() - t0
         oracle.set_threads(0)
+        # each workload's largest batch, timed on a sample of as many rows as
+        # the oracle has threads (one row per thread: every row is an
+        # independent full pass over the vocabulary) and scaled to the batch
+        per_wl = []
+        for wk, Bw in ((wl.TINY, 4), (wlk, 32), (wl.QWEN3, 256), (wl.LARGE_BATCH, 512),
+                       (wl.TP8_SHARD, 256)):
+            n_rows = min(Bw, cores)
+            Wk = W_cpu if wk is wlk else wl.bf16_bits(wl.make_w(wk, "cpu" if wk.w_bytes() < (64 << 20)
+                                                              else dev))
+            hk = wl.bf16_bits(wl.make_h(wk, Bw, "cpu"))
+            Tk = wl.make_temperature(wk, Bw, "cpu").numpy()
+            t0 = time.perf_counter()
+            oracle.sample(hk, Wk, Tk, *wk.sampler_seed(0), vocab_offset=wk.vocab_offset,
+                          rows=list(range(n_rows)))
+            dtk = time.perf_counter() - t0
+            per_wl.append({"workload": wk.name, "B": Bw, "rows_timed": n_rows,
+                           "s_per_step": round(dtk * -(-Bw // n_rows), 6)})
+            del Wk
         cpu = {"value": round(dt * 1e6 * B / len(rows), 1), "unit": "µs/step",
-               "cores": cores, "kind": "oracle",
+               "cores": cores, "kind": "oracle", "cpu_model": cpu_model(),
                "sample": f"three full decode steps of the B={B} workload (all {len(rows)} rows, "
                          f"full V={V}, fp64 dot products), median {dt:.2f} s wall",
-               "single_thread_b1_us_per_step": round(dt1 * 1e6, 1)}
+               "single_thread_b1_us_per_step": round(dt1 * 1e6, 1),
+               "per_workload": per_wl}
 
     line = {
         "metric": METRIC, "value": round(us, 2), "unit": "µs/step", "n_gpus": 1,
@@ -452,9 +544,13 @@ def main():
                      "traffic": measured_traffic(B, head_cfg),
                      "kernel": head_cfg,
                      "kernel_sources_sha256": kernel_sources_sha256()[:16],
-                     "kernel_avg_us": round(k_us, 2), "kernel_min_us": round(k_lo * 1e3, 2),
-                     "kernel_max_us": round(k_hi * 1e3, 2), "kernel_launches": k_n,
+                     "launch_bracket_avg_us": round(k_us, 2),
+                     "launch_bracket_min_us": round(k_lo * 1e3, 2),
+                     "launch_bracket_max_us": round(k_hi * 1e3, 2), "launches": k_n,
+                     "duration_source": "HIP events on the launch stream around each fused-kernel "
+                                        "launch (kernel plus its dispatch; the tile merge is outside)",
                      "algorithmic_bytes_per_launch": bytes_},
+        "us_per_step_p10_p50_p90": [round(p10, 2), round(p50, 2), round(p90, 2)],
         "row_major": row_major,
         "unfused_us_per_step": round(unf_us, 2) if unf_us is not None else None,
         "cpu_baseline": cpu,
@@ -462,8 +558,8 @@ def main():
         "grouped_lse": grouped,
         "online": online,
         "other_workloads": workloads,
-        "device": {"name": props.name, "cus": props.multi_processor_count,
-                   "gcn_arch": getattr(props, "gcnArchName", "")},
+        "device": {"name": props.name, "gcn_arch": getattr(props, "gcnArchName", ""),
+                   **device_peaks(fsl, dev)},
     }
     print(json.dumps(line), flush=True)
 

@@ -291,6 +291,11 @@ FS_API fs_status fs_debug_noise(uint64_t seed, uint64_t step, uint32_t row, uint
 FS_API fs_status fs_debug_gumbel(const uint32_t* bits, int64_t n, float* out_gumbel,
                           void* stream);
 
+/* Diagnostics: the compute-unit count and the peak shader clock (kHz) the
+ * HIP runtime reports for `device`, from which a caller derives the dense
+ * MFMA peak it measures against.  Either output may be NULL. */
+FS_API fs_status fs_device_info(int32_t device, int32_t* compute_units, int32_t* clock_khz);
+
 /* Kernel configurations of the fused sampler.  fs_force_config(id) pins
  * every later fs_sample call in the process to configuration id (0 ..
  * fs_num_configs() - 1); id = -1 restores the automatic choice.  Results do

@@ -76,6 +76,8 @@ def lib():
                                      vp, vp, vp, sz, vp], ctypes.c_int),
         ("fs_debug_noise", [u64, u64, u32, u32, i64, vp, vp, vp], ctypes.c_int),
         ("fs_debug_gumbel", [vp, i64, vp, vp], ctypes.c_int),
+        ("fs_device_info", [i32, ctypes.POINTER(ctypes.c_int32), ctypes.POINTER(ctypes.c_int32)],
+         ctypes.c_int),
         ("fs_num_configs", [], i32),
         ("fs_config_name", [i32], ctypes.c_char_p),
         ("fs_force_config", [i32], ctypes.c_int),
@@ -431,6 +433,13 @@ def debug_gumbel(bits: torch.Tensor):
     g = torch.empty(bits.shape[0], dtype=torch.float32, device=bits.device)
     _check(lib().fs_debug_gumbel(_ptr(bits), bits.shape[0], _ptr(g), _stream(bits.device)))
     return g
+
+
+def device_info(device: int = 0):
+    """(compute units, peak shader clock in kHz) the HIP runtime reports."""
+    cus, clk = ctypes.c_int32(0), ctypes.c_int32(0)
+    _check(lib().fs_device_info(int(device), ctypes.byref(cus), ctypes.byref(clk)))
+    return cus.value, clk.value
 
 
 def profile_enable(capacity: int):

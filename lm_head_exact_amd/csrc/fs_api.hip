@@ -642,6 +642,23 @@ fs_status fs_profile_read(int32_t* launches, double* total_ms, double* min_ms,
   return FS_OK;
 }
 
+fs_status fs_device_info(int32_t device, int32_t* compute_units, int32_t* clock_khz) {
+  if (device < 0) return fail(FS_ERR_INVALID_ARG, "device must be >= 0 (got %d)", device);
+  int v = 0;
+  hipError_t e;
+  if (compute_units) {
+    if ((e = hipDeviceGetAttribute(&v, hipDeviceAttributeMultiprocessorCount, device)) != hipSuccess)
+      return hip_fail(e, "hipDeviceGetAttribute(MultiprocessorCount)");
+    *compute_units = v;
+  }
+  if (clock_khz) {
+    if ((e = hipDeviceGetAttribute(&v, hipDeviceAttributeClockRate, device)) != hipSuccess)
+      return hip_fail(e, "hipDeviceGetAttribute(ClockRate)");
+    *clock_khz = v;
+  }
+  return FS_OK;
+}
+
 int32_t fs_num_configs(void) { return fs::num_fused_configs(); }
 
 const char* fs_config_name(int32_t id) { return fs::fused_config_name(id); }

@@ -375,3 +375,4 @@ def test_launch_without_a_device_reports_the_runtime_error(L, monkeypatch):
     monkeypatch.delenv("FS_FAULT_INJECT", raising=False)
     assert _sample(L) == bd.FS_ERR_HIP
     assert len(L.fs_last_error()) > 0 and b"FS_FAULT_INJECT" not in L.fs_last_error()
+
