@@ -133,6 +133,23 @@ FS_API fs_status fs_sample_packed(const void* h, const void* W_packed, int32_t B
                                   float* out_maxval, void* workspace, size_t workspace_bytes,
                                   void* stream);
 
+/* fs_sample_packed without a workspace argument, for callers that cannot
+ * allocate device memory around the call (code being captured into a graph,
+ * tight serving loops, harnesses that forbid allocation).  The tile partials
+ * go to an 8 MiB array the library holds in each device's memory until the
+ * process ends; the call allocates nothing.  Its kernels and results are
+ * fs_sample_packed's.  Every call on one device shares that array, so calls
+ * that overlap on one device (concurrent streams, or several host threads)
+ * race and must be serialised by the caller.  A shape whose partials exceed
+ * the array (2 * 4 * B * ceil((V + 3) / rows) bytes, rows the chosen
+ * configuration's vocabulary rows per block: 16 for the small-batch
+ * kernels, 256 or more for the batch-tiled ones) returns FS_ERR_WORKSPACE
+ * and launches nothing; other errors as fs_sample_packed. */
+FS_API fs_status fs_sample_packed_noalloc(const void* h, const void* W_packed, int32_t B,
+                                          int32_t D, int32_t V, int32_t vocab_offset,
+                                          const float* temperature, uint64_t seed, uint64_t step,
+                                          int32_t* out_ids, float* out_maxval, void* stream);
+
 /* One vocabulary shard's contribution for the grouped / tensor-parallel flow
  * (wiki summary, "Method": each rank reduces its own shard to a per-row
  * (local max, local argmax) pair, and only those pairs are exchanged).

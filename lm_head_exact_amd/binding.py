@@ -66,6 +66,8 @@ def lib():
         ("fs_packed_weights_bytes", [i32, i32, i32], sz),
         ("fs_pack_weights", [vp, i32, i32, i32, vp, sz, vp], ctypes.c_int),
         ("fs_sample_packed", sample_args, ctypes.c_int),
+        ("fs_sample_packed_noalloc", [vp, vp, i32, i32, i32, i32, vp, u64, u64, vp, vp, vp],
+         ctypes.c_int),
         ("fs_online_bounds_workspace_bytes", [i32, i32], sz),
         ("fs_online_workspace_bytes", [i32, i32, i32, i32], sz),
         ("fs_online_bounds", [vp, i32, i32, vp, i32, vp, vp, sz, vp], ctypes.c_int),
@@ -327,6 +329,35 @@ def sample_packed(h: torch.Tensor, W_packed: torch.Tensor, V: int, temperature: 
                                   _ptr(temperature), int(seed) & (2**64 - 1),
                                   int(step) & (2**64 - 1), _ptr(ids), _ptr(val), _ptr(workspace),
                                   workspace.numel() * workspace.element_size(), _stream(dev)))
+    return ids, val
+
+
+def sample_packed_noalloc(h: torch.Tensor, W_packed: torch.Tensor, V: int,
+                          temperature: torch.Tensor, seed: int, step: int, vocab_offset: int = 0,
+                          out=None):
+    """fs_sample_packed_noalloc: sample_packed with the tile partials in the
+    library's own per-device scratch array instead of a workspace (calls that
+    overlap on one device race).  Allocates nothing when `out` is given."""
+    _req(h, "h", torch.bfloat16, 2)
+    _req(W_packed, "W_packed", torch.bfloat16, 1)
+    _req(temperature, "temperature", torch.float32, 1)
+    B, D = h.shape
+    need = packed_weights_bytes(V, D, vocab_offset)
+    if need == 0 or W_packed.numel() * 2 < need:
+        raise ValueError(f"W_packed holds {W_packed.numel() * 2} bytes; {need} needed")
+    if temperature.shape[0] != B:
+        raise ValueError("temperature must have B entries")
+    dev = h.device
+    if out is None:
+        out = (torch.empty(B, dtype=torch.int32, device=dev),
+               torch.empty(B, dtype=torch.float32, device=dev))
+    ids, val = out
+    if len({t.device for t in (h, W_packed, temperature, ids, val)}) != 1:
+        raise ValueError("all tensors must be on one device")
+    _check(lib().fs_sample_packed_noalloc(_ptr(h), _ptr(W_packed), B, D, V, int(vocab_offset),
+                                          _ptr(temperature), int(seed) & (2**64 - 1),
+                                          int(step) & (2**64 - 1), _ptr(ids), _ptr(val),
+                                          _stream(dev)))
     return ids, val
 
 

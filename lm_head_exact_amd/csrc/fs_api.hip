@@ -80,6 +80,9 @@ fs_status check_shape(int32_t B, int32_t D, int32_t V, int32_t vocab_offset) {
   return FS_OK;
 }
 
+// workspace == kNoWorkspace: the call uses the library's scratch array.
+const void* const kNoWorkspace = reinterpret_cast<const void*>(~uintptr_t{0} & ~uintptr_t{255});
+
 fs_status check_sample_args(const void* h, const void* W, int32_t B, int32_t D, int32_t V,
                             int32_t vocab_offset, const float* temperature, const void* out_a,
                             const void* out_b, const void* workspace) {
@@ -92,6 +95,41 @@ fs_status check_sample_args(const void* h, const void* W, int32_t B, int32_t D, 
   if (!aligned(temperature, 4) || !aligned(out_a, 4) || !aligned(out_b, 4))
     return fail(FS_ERR_INVALID_ARG, "temperature and outputs must be 4-byte aligned");
   if (!aligned(workspace, 256)) return fail(FS_ERR_INVALID_ARG, "workspace must be 256-byte aligned");
+  return FS_OK;
+}
+
+// ---- scratch array of the allocation-free entry point ----
+// Tile partials of fs_sample_packed_noalloc live here instead of in a caller
+// workspace.  Each device the library runs on holds its own copy until the
+// process ends; every call on a device shares it, so calls that overlap on
+// one device race.  Nothing in it needs to start at zero: a call writes every
+// partial it reads.
+constexpr size_t kScratchBytes = size_t{8} << 20;
+static __device__ __align__(256) unsigned char scratch[kScratchBytes];
+
+// Device address of `scratch` on the current device, looked up once per
+// device (the array's name is a host-side stand-in, not a device address).
+fs_status scratch_address(void** out) {
+  constexpr int kMaxDevices = 64;
+  static std::atomic<void*> addr[kMaxDevices];
+  static std::mutex mu;
+  int dev = 0;
+  hipError_t e = hipGetDevice(&dev);
+  if (e != hipSuccess) return hip_fail(e, "hipGetDevice");
+  if (dev < 0 || dev >= kMaxDevices)
+    return fail(FS_ERR_UNSUPPORTED, "device %d beyond the %d the scratch table covers", dev,
+                kMaxDevices);
+  void* p = addr[dev].load(std::memory_order_acquire);
+  if (p == nullptr) {
+    std::lock_guard<std::mutex> lock(mu);
+    p = addr[dev].load(std::memory_order_relaxed);
+    if (p == nullptr) {
+      e = hipGetSymbolAddress(&p, HIP_SYMBOL(scratch));
+      if (e != hipSuccess) return hip_fail(e, "hipGetSymbolAddress(scratch)");
+      addr[dev].store(p, std::memory_order_release);
+    }
+  }
+  *out = p;
   return FS_OK;
 }
 
@@ -140,7 +178,7 @@ fs_status run_fused(const void* h, const void* W, int32_t B, int32_t D, int32_t 
                                   workspace);
   if (s != FS_OK || B == 0) return s;
   const size_t need = fused_workspace(B, V);
-  if (workspace_bytes < need)
+  if (workspace != kNoWorkspace && workspace_bytes < need)
     return fail(FS_ERR_WORKSPACE, "%s: workspace of %zu bytes is below the %zu required", who,
                 workspace_bytes, need);
   if (w_packed && D % 32 != 0)
@@ -155,8 +193,25 @@ fs_status run_fused(const void* h, const void* W, int32_t B, int32_t D, int32_t 
   if (w_packed && !fs::fused_config_reads_packed(cfg))
     return fail(FS_ERR_UNSUPPORTED, "%s: configuration %s for B=%d, D=%d, V=%d has no packed-W kernel",
                 who, config_label(cfg), B, D, V);
-  if (launch_fault_injected()) return injected_failure(who);
-  const size_t S = max_splits(V);
+  // Split capacity of the partial layout: a caller workspace is sized for the
+  // most splits any configuration can launch; the scratch array for the
+  // chosen configuration's (blocks of its row count over a grid shifted by
+  // fewer than 4 rows).
+  size_t S = max_splits(V);
+  if (workspace == kNoWorkspace) {
+    const size_t rows = static_cast<size_t>(fs::fused_rows_per_block(cfg));
+    S = (static_cast<size_t>(V) + 3 + rows - 1) / rows;
+    const size_t need = (out_lse ? 3 : 2) * fs::round_up(sizeof(float) * B * S, 256);
+    if (need > kScratchBytes)
+      return fail(FS_ERR_WORKSPACE,
+                  "%s: B=%d, V=%d needs %zu bytes of partials, beyond the %zu-byte scratch array",
+                  who, B, V, need, kScratchBytes);
+    if (launch_fault_injected()) return injected_failure(who);
+    const fs_status st = scratch_address(&workspace);
+    if (st != FS_OK) return st;
+  } else if (launch_fault_injected()) {
+    return injected_failure(who);
+  }
   fs::SampleArgs a;
   a.h = static_cast<const __bf16*>(h);
   a.W = static_cast<const __bf16*>(W);
@@ -417,6 +472,15 @@ fs_status fs_sample_packed(const void* h, const void* W_packed, int32_t B, int32
   return run_fused(h, W_packed, B, D, V, vocab_offset, temperature, seed, step, out_ids,
                    out_maxval, nullptr, workspace, workspace_bytes, stream, "fs_sample_packed",
                    true);
+}
+
+fs_status fs_sample_packed_noalloc(const void* h, const void* W_packed, int32_t B, int32_t D,
+                                   int32_t V, int32_t vocab_offset, const float* temperature,
+                                   uint64_t seed, uint64_t step, int32_t* out_ids,
+                                   float* out_maxval, void* stream) {
+  return run_fused(h, W_packed, B, D, V, vocab_offset, temperature, seed, step, out_ids,
+                   out_maxval, nullptr, const_cast<void*>(kNoWorkspace), 0, stream,
+                   "fs_sample_packed_noalloc", true);
 }
 
 fs_status fs_sample_partial(const void* h, const void* W, int32_t B, int32_t D, int32_t V,

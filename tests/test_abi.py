@@ -345,6 +345,8 @@ def test_injected_launch_failure_every_entry_point(L, inject):
         "fs_sample": lambda: _sample(L, "fs_sample"),
         "fs_sample_partial": lambda: _sample(L, "fs_sample_partial"),
         "fs_sample_packed": lambda: _sample(L, "fs_sample_packed"),
+        "fs_sample_packed_noalloc": lambda: L.fs_sample_packed_noalloc(A, A, 4, 256, 1000, 0, A, 1,
+                                                                       2, A, A, None),
         "fs_sample_unfused": lambda: _sample(L, "fs_sample_unfused"),
         "fs_sample_partial_lse": lambda: _sample_lse(L),
         "fs_merge": lambda: L.fs_merge(A, A, 3, 4, A, A, None),
@@ -376,3 +378,29 @@ def test_launch_without_a_device_reports_the_runtime_error(L, monkeypatch):
     assert _sample(L) == bd.FS_ERR_HIP
     assert len(L.fs_last_error()) > 0 and b"FS_FAULT_INJECT" not in L.fs_last_error()
 
+
+def _noalloc(L, h=ALIGNED, W=ALIGNED, B=4, D=256, V=1000, off=0, T=ALIGNED, ids=ALIGNED,
+             val=ALIGNED):
+    return L.fs_sample_packed_noalloc(h, W, B, D, V, off, T, 1, 2, ids, val, None)
+
+
+@pytest.mark.parametrize("kw,status", [
+    (dict(D=7), bd.FS_ERR_INVALID_ARG),
+    (dict(D=72), bd.FS_ERR_INVALID_ARG),            # packed weights need D % 32 == 0
+    (dict(V=0), bd.FS_ERR_INVALID_ARG),
+    (dict(B=-1), bd.FS_ERR_INVALID_ARG),
+    (dict(h=None), bd.FS_ERR_INVALID_ARG),
+    (dict(T=ALIGNED + 2), bd.FS_ERR_INVALID_ARG),
+    (dict(W=ALIGNED + 8), bd.FS_ERR_INVALID_ARG),
+    (dict(B=16 * 65535 + 1), bd.FS_ERR_UNSUPPORTED),
+    # partials beyond the 8 MiB scratch array, refused before any launch
+    (dict(B=2048, V=200000), bd.FS_ERR_WORKSPACE),
+    (dict(B=1 << 19, V=1 << 20), bd.FS_ERR_WORKSPACE),
+    (dict(B=0, h=None, W=None, T=None, ids=None, val=None), bd.FS_OK),
+])
+def test_noalloc_argument_errors(L, kw, status):
+    assert _noalloc(L, **kw) == status
+    if status != bd.FS_OK:
+        assert len(L.fs_last_error()) > 0
+    if status == bd.FS_ERR_WORKSPACE:
+        assert b"scratch" in L.fs_last_error()
