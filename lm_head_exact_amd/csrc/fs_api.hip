@@ -746,7 +746,12 @@ int32_t fs_selected_config_packed(int32_t B, int32_t D, int32_t V) {
 }
 
 const char* fs_status_string(fs_status s) {
-  switch (s) {
+  // A caller may pass any int: read the code's bits instead of loading an
+  // enum value outside its range (undefined behaviour in C++).
+  static_assert(sizeof(fs_status) == sizeof(int), "status is int-sized");
+  int code;
+  std::memcpy(&code, &s, sizeof code);
+  switch (code) {
     case FS_OK: return "FS_OK";
     case FS_ERR_INVALID_ARG: return "FS_ERR_INVALID_ARG";
     case FS_ERR_UNSUPPORTED: return "FS_ERR_UNSUPPORTED";
