@@ -11,7 +11,6 @@ int fused_configs_dma_a(const FusedConfig** out) {
       FS_DMAG(2, 16, 8, 64, 4, 4, 4, 2),  // B > 128 (batch blocks of 256)
       FS_DMAG(2, 16, 8, 128, 4, 2, 4, 2),
       FS_DMAP(2, 16, 8, 128, 4, 2, 4, 2), // B > 256 (several batch blocks)
-      FS_DMAP(2, 16, 8, 64, 4, 4, 4, 2),  // B > 256 on packed W (its non-temporal twin)
   };
   *out = k;
   return static_cast<int>(sizeof(k) / sizeof(k[0]));

@@ -8,8 +8,6 @@ namespace fs {
 int fused_configs_dma_ntl(const FusedConfig** out) {
   static const FusedConfig k[] = {
       FS_DMAN(2, 16, 8, 64, 4, 4, 4, 2),
-      FS_DMAN(2, 16, 8, 128, 4, 2, 4, 2),
-      FS_DMAPN(2, 16, 8, 128, 4, 2, 4, 2),
       FS_DMAN(4, 4, 8, 64, 4, 3, 4, 2),
       FS_DMAN(4, 8, 8, 64, 4, 3, 4, 2),
       FS_DMAN(5, 4, 8, 64, 4, 3, 4, 2),

@@ -9,8 +9,6 @@ int fused_configs_lds(const FusedConfig** out) {
       FS_LDS(2, 4, 4, 64, 4, 0),        // B <= 64 when the DMA grid would leave CUs idle
       FS_LDSR(4, 8, 4, 64, 4, 1, 4),    // B <= 128, likewise
       FS_LDSR(2, 16, 4, 64, 4, 1, 4),   // B > 128, likewise
-      FS_LDS(2, 16, 4, 64, 4, 0),       // B > 128 when 2*B*D >= 2^31
-      FS_LDS(2, 8, 4, 64, 8, 0),
       FS_LDSR(2, 8, 4, 64, 8, 1, 4),
   };
   *out = k;

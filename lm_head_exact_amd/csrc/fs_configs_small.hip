@@ -9,19 +9,10 @@ int fused_configs_small(const FusedConfig** out) {
       FS_PERSIST(1, 8, 16, 8),   // D = 4096, B <= 16
       FS_PERSIST(2, 8, 16, 8),   // D = 4096, B <= 32
       FS_PERSIST(1, 8, 32, 8),   // D = 8192, B <= 16
-      FS_PERSIST(1, 4, 2, 2),    // D = 256 (small shapes)
-      FS_PERSIST(2, 4, 2, 2),    // D = 256
       FS_KSPLIT(1, 1, 4, 8, 0),  // B <= 8 when no persistent shape fits
       FS_STREAM(4, 1, 4, 4, 0),  // any D: fallback for B <= 16
       FS_STREAM(2, 4, 4, 4, 0),  // any D: fallback for larger B
-      FS_PERSIST(1, 8, 16, 16),
-      FS_KSPLIT(2, 1, 4, 8, 0),
-      FS_KSPLIT(4, 2, 4, 4, 0),
-      FS_STREAM(1, 1, 4, 8, 0),
-      FS_PERSISTN(1, 8, 16, 8),
-      FS_PERSISTN(2, 8, 16, 8),
-      FS_PERSISTN(1, 8, 32, 8),
-      FS_PERSISTN(1, 8, 16, 16),  // packed W: tuning alternative
+      FS_PERSISTN(1, 8, 32, 8),   // packed W, D = 8192, B <= 16
       FS_PERSISTN(2, 8, 16, 4),   // packed W, B <= 32
       FS_PERSISTN(1, 16, 8, 4),   // packed W, B <= 16
   };

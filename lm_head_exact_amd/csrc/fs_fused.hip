@@ -262,14 +262,14 @@ static int auto_config_shape(int32_t B, int32_t D, int32_t V, bool packed) {
   static const int dma256 = config_id("dma_mr2_nt16_nw8_kc64_p4_s4_br4_g2");
   static const int dma256_kc128 = config_id("dma_mr2_nt16_nw8_kc128_p4_s2_br4_g2");
   static const int dma_paired = config_id("dmapair_mr2_nt16_nw8_kc128_p4_s2_br4_g2");
-  static const int dma_paired_kc64 = config_id("dmapair_mr2_nt16_nw8_kc64_p4_s4_br4_g2");
+  // (packed W only: named by its non-temporal form, the one the packed choice takes)
+  static const int dma_paired_kc64 = config_id("dmapair_mr2_nt16_nw8_kc64_p4_s4_br4_g2_ntl1");
   static const int dma64_short = config_id("dma_mr1_nt4_nw4_kc64_p8_s3_br4_g2");
   static const int dma128_short = config_id("dma_mr1_nt8_nw4_kc64_p8_s3_br4_g2");
   static const int dma256_short = config_id("dma_mr1_nt16_nw4_kc64_p8_s3_br4_g2");
   static const int lds64 = config_id("lds_mr2_nt4_nw4_kc64_p4_ntl0");
   static const int lds128 = config_id("lds_mr4_nt8_nw4_kc64_p4_wb1_br4");
   static const int lds256 = config_id("lds_mr2_nt16_nw4_kc64_p4_wb1_br4");
-  static const int lds_big = config_id("lds_mr2_nt16_nw4_kc64_p4_ntl0");
   static const int lds_narrow = config_id("lds_mr2_nt8_nw4_kc64_p8_wb1_br4");
   static const int stream_small = config_id("stream_mr4_nt1_nw4_p4_ntl0");
   static const int stream_big = config_id("stream_mr2_nt4_nw4_p4_ntl0");
@@ -322,7 +322,6 @@ static int auto_config_shape(int32_t B, int32_t D, int32_t V, bool packed) {
   if (short_v && fused_config_supports(p.dma_short, B, D)) return p.dma_short;
   if (short_v && B > 128 && fused_config_supports(lds_narrow, B, D)) return lds_narrow;
   if (fused_config_supports(p.lds, B, D)) return p.lds;
-  if (B > 64 && fused_config_supports(lds_big, B, D)) return lds_big;
   return B <= 16 ? stream_small : stream_big;
 }
 
