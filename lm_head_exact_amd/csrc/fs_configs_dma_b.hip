@@ -11,7 +11,6 @@ int fused_configs_dma_b(const FusedConfig** out) {
       FS_DMAG(5, 4, 8, 64, 4, 3, 4, 2),   // B <= 64, 640-row blocks
       FS_DMAG(5, 8, 8, 64, 2, 3, 4, 2),   // B <= 128, 640-row blocks
       FS_DMAG(1, 4, 4, 64, 8, 3, 4, 2),   // short vocabularies: 64-row blocks
-      FS_DMAG(1, 16, 4, 64, 8, 3, 4, 2),
       FS_DMAG(1, 8, 4, 64, 8, 3, 4, 2),
 #ifdef FS_TUNING_SWEEPS
       FS_DMA(2, 16, 8, 64, 4, 4, 4),

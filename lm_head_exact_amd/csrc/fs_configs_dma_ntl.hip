@@ -14,8 +14,8 @@ int fused_configs_dma_ntl(const FusedConfig** out) {
       FS_DMAN(5, 8, 8, 64, 2, 3, 4, 2),
       FS_DMAN(1, 4, 4, 64, 8, 3, 4, 2),
       FS_DMAN(1, 8, 4, 64, 8, 3, 4, 2),
-      FS_DMAN(1, 16, 4, 64, 8, 3, 4, 2),
       FS_DMAPN(2, 16, 8, 64, 4, 4, 4, 2),
+      FS_DMAPN(1, 8, 8, 128, 8, 3, 4, 2),
   };
   *out = k;
   return static_cast<int>(sizeof(k) / sizeof(k[0]));
