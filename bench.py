@@ -322,8 +322,10 @@ def main():
             del ukp
         sweep.append(entry)
         del kp
-    # Grouped (hierarchical) sampler: the vocabulary as G contiguous groups,
-    # one fs_sample_partial_lse per group into its slot, then fs_merge_lse.
+    # Grouped (hierarchical) sampler: the vocabulary as G contiguous groups.
+    # One step is fs_sample_groups_lse (every group's partials in one launch)
+    # then fs_merge_lse; the same step as G fs_sample_partial_lse launches
+    # (one per group) is timed beside it.
     grouped = []
     for b, G in ((B, 1), (B, 8), (256, 1), (256, 8)):
         if args.no_grouped or G < 1 or V % G:
@@ -333,39 +335,57 @@ def main():
         pv = torch.empty(G, b, dtype=torch.float32, device=dev)
         pi = torch.empty(G, b, dtype=torch.int32, device=dev)
         pl = torch.empty(G, b, dtype=torch.float32, device=dev)
-        ws = fsl.alloc_workspace(fsl.workspace_bytes(b, D, V // G), dev)
+        Vg = V // G
+        cuts = [p * Vg for p in range(G + 1)]
+        ws1 = fsl.alloc_workspace(fsl.groups_workspace_bytes(b, D, V, G), dev)
+        wsg = fsl.alloc_workspace(fsl.workspace_bytes(b, D, Vg), dev)
         outs = (torch.empty(b, dtype=torch.int32, device=dev),
                 torch.empty(b, dtype=torch.float32, device=dev),
                 torch.empty(b, dtype=torch.float32, device=dev))
-        Vg = V // G
+        W_g = Wp if Wp is not None else W
 
-        def gfn(i, h_g=h_g, T_g=T_g, pv=pv, pi=pi, pl=pl, ws=ws, outs=outs, G=G, Vg=Vg):
+        def one(i, h_g=h_g, T_g=T_g, pv=pv, pi=pi, pl=pl, ws1=ws1, outs=outs, cuts=cuts):
+            seed, step = wlk.sampler_seed(i)
+            fsl.sample_groups_lse(h_g, W_g, T_g, seed, step, cuts, out=(pv, pi, pl),
+                                  workspace=ws1, V=V)
+            fsl.merge_lse(pv, pi, pl, T_g, seed, step, out=outs)
+
+        def sep(i, h_g=h_g, T_g=T_g, pv=pv, pi=pi, pl=pl, wsg=wsg, outs=outs, G=G, Vg=Vg):
             seed, step = wlk.sampler_seed(i)
             for p in range(G):
                 if Wp is not None:  # group p of the fragment-order W (Vg % 16 == 0)
                     fsl.sample_partial_lse(h_g, Wp[p * Vg * D:(p + 1) * Vg * D], T_g, seed, step,
-                                           p * Vg, pv[p], pi[p], pl[p], workspace=ws, V=Vg)
+                                           p * Vg, pv[p], pi[p], pl[p], workspace=wsg, V=Vg)
                 else:
                     fsl.sample_partial_lse(h_g, W[p * Vg:(p + 1) * Vg], T_g, seed, step, p * Vg,
-                                           pv[p], pi[p], pl[p], workspace=ws)
+                                           pv[p], pi[p], pl[p], workspace=wsg)
             fsl.merge_lse(pv, pi, pl, T_g, seed, step, out=outs)
-        # one step is G + 1 small launches: replay it as a captured graph so that
-        # host-side call overhead does not stand in for device time
-        for i in range(3):
-            gfn(i)
-        torch.cuda.synchronize()
-        graph = torch.cuda.CUDAGraph()
-        with torch.cuda.graph(graph):
-            gfn(7)
-        gt = time_steps(torch, lambda i: graph.replay(), max(10, args.sweep_steps // 2), 5,
-                        torch.cuda.current_stream(dev)) * 1e3
-        del graph
+        # replayed as captured graphs so that host-side call overhead does not
+        # stand in for device time
+        times = {}
+        for name, fn in (("one_launch", one), ("per_group_launches", sep)):
+            for i in range(3):
+                fn(i)
+            torch.cuda.synchronize()
+            graph = torch.cuda.CUDAGraph()
+            with torch.cuda.graph(graph):
+                fn(7)
+            times[name] = time_steps(torch, lambda i: graph.replay(),
+                                     max(10, args.sweep_steps // 2), 5,
+                                     torch.cuda.current_stream(dev)) * 1e3
+            torch.cuda.synchronize()
+            del graph
         plain = next((e.get("packed_us_per_step" if Wp is not None else "us_per_step")
                       for e in sweep if e["B"] == b), None)
-        grouped.append({"B": b, "groups": G, "us_per_step": round(gt, 2),
+        cfg = fsl.selected_config(b, D, V, packed=Wp is not None, tiled=True)
+        grouped.append({"B": b, "groups": G, "us_per_step": round(times["one_launch"], 2),
+                        "per_group_launches_us_per_step": round(times["per_group_launches"], 2),
+                        "config": fsl.config_name(cfg),
                         "w_layout": "fragment order" if Wp is not None else "row-major",
-                        "whole_vocabulary_us_per_step": plain})
-        del h_g, T_g, pv, pi, pl, ws, outs
+                        "whole_vocabulary_us_per_step": plain,
+                        "ratio_to_whole_vocabulary": (round(times["one_launch"] / plain, 3)
+                                                      if plain else None)})
+        del h_g, T_g, pv, pi, pl, ws1, wsg, outs
 
     # Online sampler with early finalisation: fs_sample_online per step over
     # the vocabulary in 8 chunks of 16032 rows, or in 2 chunks (the first

@@ -197,6 +197,40 @@ FS_API fs_status fs_sample_partial_lse_packed(const void* h, const void* W_packe
                                               void* workspace, size_t workspace_bytes,
                                               void* stream);
 
+/* The grouped sampler's per-group partials for G groups in one launch.  The
+ * vocabulary W[0 .. V) is split at the HOST array cuts (0 = cuts[0] <
+ * cuts[1] < ... < cuts[G] = V, 1 <= G <= 64); slot g of the outputs (element
+ * g * B + b of partial_val / partial_idx / partial_lse, [G][B] part-major as
+ * fs_merge_lse reads them) holds what fs_sample_partial_lse would return over
+ * W rows [cuts[g], cuts[g+1]) at vocab_offset + cuts[g]: the group's
+ * Gumbel-max (value, global id) and its log-sum-exp.  One fused launch covers
+ * every group (each group's vocabulary blocks start at its own first row, so
+ * no block mixes two groups) and one merge launch fills the slots, instead
+ * of G launches each over a slice too short to fill the device.  It runs the
+ * tiled kernel configurations only (a forced persistent configuration is
+ * FS_ERR_UNSUPPORTED); within one summation order the slots equal the
+ * separate calls bit for bit.
+ *   workspace   >= fs_groups_workspace_bytes(B, D, V, G) bytes (0 for invalid
+ *               arguments); contents on entry ignored
+ * Errors as fs_sample_partial_lse; a cuts array that does not partition
+ * [0, V) or G outside [1, 64] is FS_ERR_INVALID_ARG.  The _packed form reads
+ * fragment-order W (fs_pack_weights at the same vocab_offset mod 4) and needs
+ * every group start cuts[g] (0 < g < G) to be a multiple of 16. */
+FS_API size_t fs_groups_workspace_bytes(int32_t B, int32_t D, int32_t V, int32_t n_groups);
+FS_API fs_status fs_sample_groups_lse(const void* h, const void* W, int32_t B, int32_t D,
+                                      int32_t V, int32_t vocab_offset, const float* temperature,
+                                      uint64_t seed, uint64_t step, const int32_t* cuts,
+                                      int32_t n_groups, float* partial_val, int32_t* partial_idx,
+                                      float* partial_lse, void* workspace,
+                                      size_t workspace_bytes, void* stream);
+FS_API fs_status fs_sample_groups_lse_packed(const void* h, const void* W_packed, int32_t B,
+                                             int32_t D, int32_t V, int32_t vocab_offset,
+                                             const float* temperature, uint64_t seed,
+                                             uint64_t step, const int32_t* cuts, int32_t n_groups,
+                                             float* partial_val, int32_t* partial_idx,
+                                             float* partial_lse, void* workspace,
+                                             size_t workspace_bytes, void* stream);
+
 /* Grouped merge: the categorical distribution factorises as
  * P(i) = P(G) P(i | G) with P(G) proportional to exp(LSE_G), and each
  * group's partial already holds a sample of P(i | G).
@@ -320,10 +354,13 @@ FS_API fs_status fs_device_info(int32_t device, int32_t* compute_units, int32_t*
 FS_API int32_t fs_num_configs(void);
 FS_API const char* fs_config_name(int32_t id);
 FS_API fs_status fs_force_config(int32_t id);
-/* Configuration fs_sample would use for batch size B (after forcing), and
- * the one fs_sample_packed would use. */
+/* Configuration fs_sample would use for batch size B (after forcing), the
+ * one fs_sample_packed would use, and the one fs_sample_groups_lse (packed
+ * != 0: fs_sample_groups_lse_packed) would use over a V-row vocabulary.
+ * -1 for an invalid shape. */
 FS_API int32_t fs_selected_config(int32_t B, int32_t D, int32_t V);
 FS_API int32_t fs_selected_config_packed(int32_t B, int32_t D, int32_t V);
+FS_API int32_t fs_selected_config_groups(int32_t B, int32_t D, int32_t V, int32_t packed);
 
 /* Profiling of the fused kernel.  fs_profile_enable(capacity) creates
  * 2 * capacity HIP events (outside any sampling call); while enabled, each of

@@ -11,7 +11,8 @@ _BINDING_NAMES = ("sample", "sample_partial", "merge", "sample_partial_lse", "me
                   "num_configs", "config_name", "profile_enable", "profile_read", "force_config", "selected_config",
                   "FlashSampleError", "alloc_workspace", "online_bounds", "sample_online",
                   "online_workspace_bytes", "pack_weights", "sample_packed",
-                  "packed_weights_bytes", "device_info", "sample_packed_noalloc")
+                  "packed_weights_bytes", "device_info", "sample_packed_noalloc",
+                  "sample_groups_lse", "groups_workspace_bytes")
 __all__ = list(_BINDING_NAMES)
 
 

@@ -63,6 +63,11 @@ def lib():
         ("fs_sample_partial_lse_packed", [vp, vp, i32, i32, i32, i32, vp, u64, u64, vp, vp, vp,
                                           vp, sz, vp], ctypes.c_int),
         ("fs_merge_lse", [vp, vp, vp, i32, i32, vp, u64, u64, vp, vp, vp, vp], ctypes.c_int),
+        ("fs_groups_workspace_bytes", [i32, i32, i32, i32], sz),
+        ("fs_sample_groups_lse", [vp, vp, i32, i32, i32, i32, vp, u64, u64, vp, i32, vp, vp, vp,
+                                  vp, sz, vp], ctypes.c_int),
+        ("fs_sample_groups_lse_packed", [vp, vp, i32, i32, i32, i32, vp, u64, u64, vp, i32, vp,
+                                         vp, vp, vp, sz, vp], ctypes.c_int),
         ("fs_packed_weights_bytes", [i32, i32, i32], sz),
         ("fs_pack_weights", [vp, i32, i32, i32, vp, sz, vp], ctypes.c_int),
         ("fs_sample_packed", sample_args, ctypes.c_int),
@@ -85,6 +90,7 @@ def lib():
         ("fs_force_config", [i32], ctypes.c_int),
         ("fs_selected_config", [i32, i32, i32], i32),
         ("fs_selected_config_packed", [i32, i32, i32], i32),
+        ("fs_selected_config_groups", [i32, i32, i32, i32], i32),
         ("fs_profile_enable", [i32], ctypes.c_int),
         ("fs_profile_read", [ctypes.POINTER(ctypes.c_int32)] + [ctypes.POINTER(ctypes.c_double)] * 3,
          ctypes.c_int),
@@ -229,6 +235,47 @@ def sample_partial_lse(h, W, temperature, seed, step, vocab_offset, partial_val,
         _ptr(partial_lse), _ptr(workspace), workspace.numel() * workspace.element_size(),
         _stream(h.device)))
     return partial_val, partial_idx, partial_lse
+
+
+def groups_workspace_bytes(B: int, D: int, V: int, n_groups: int) -> int:
+    return int(lib().fs_groups_workspace_bytes(B, D, V, n_groups))
+
+
+def sample_groups_lse(h: torch.Tensor, W: torch.Tensor, temperature: torch.Tensor, seed: int,
+                      step: int, cuts, vocab_offset: int = 0, out=None, workspace=None,
+                      V: Optional[int] = None):
+    """fs_sample_groups_lse: the grouped sampler's per-group partials for the
+    groups W[cuts[g]:cuts[g+1]] in one launch.  Returns (val fp32 [G][B],
+    idx int32 [G][B], lse fp32 [G][B]), slot g as fs_sample_partial_lse over
+    group g.  W is the row-major V x D matrix, or (1-D, V given) its
+    fragment-order copy (group starts multiples of 16)."""
+    packed = W.dim() == 1
+    _req(h, "h", torch.bfloat16, 2)
+    _req(W, "W", torch.bfloat16, 1 if packed else 2)
+    _req(temperature, "temperature", torch.float32, 1)
+    B, D = h.shape
+    if packed:
+        if V is None:
+            raise ValueError("V is required with fragment-order W")
+    else:
+        V = W.shape[0]
+        if W.shape[1] != D:
+            raise ValueError("h and W must have the same D")
+    c, G = _host_cuts(cuts)
+    dev = h.device
+    if out is None:
+        out = (torch.empty(G, B, dtype=torch.float32, device=dev),
+               torch.empty(G, B, dtype=torch.int32, device=dev),
+               torch.empty(G, B, dtype=torch.float32, device=dev))
+    pv, pi, pl = out
+    if workspace is None:
+        workspace = alloc_workspace(groups_workspace_bytes(B, D, V, G), dev)
+    fn = lib().fs_sample_groups_lse_packed if packed else lib().fs_sample_groups_lse
+    _check(fn(_ptr(h), _ptr(W), B, D, V, int(vocab_offset), _ptr(temperature),
+              int(seed) & (2**64 - 1), int(step) & (2**64 - 1), c, G, _ptr(pv), _ptr(pi),
+              _ptr(pl), _ptr(workspace), workspace.numel() * workspace.element_size(),
+              _stream(dev)))
+    return pv, pi, pl
 
 
 def merge_lse(partial_val, partial_idx, partial_lse, temperature, seed, step, out=None):
@@ -500,7 +547,10 @@ def force_config(i: int):
     _check(lib().fs_force_config(int(i)))
 
 
-def selected_config(B: int, D: int, V: int, packed: bool = False) -> int:
-    """Configuration fs_sample (packed: fs_sample_packed) would use."""
+def selected_config(B: int, D: int, V: int, packed: bool = False, tiled: bool = False) -> int:
+    """Configuration fs_sample (packed: fs_sample_packed) would use; tiled:
+    the one fs_sample_groups_lse (or its packed form) would use."""
+    if tiled:
+        return int(lib().fs_selected_config_groups(B, D, V, int(packed)))
     fn = lib().fs_selected_config_packed if packed else lib().fs_selected_config
     return int(fn(B, D, V))

@@ -160,9 +160,9 @@ void destroy_events() {
   g_prof.used = 0;
 }
 
-int choose_config(int32_t B, int32_t D, int32_t V, bool packed = false) {
+int choose_config(int32_t B, int32_t D, int32_t V, bool packed = false, bool tiled = false) {
   const int forced = g_forced_config.load(std::memory_order_relaxed);
-  return forced >= 0 ? forced : fs::fused_auto_config(B, D, V, packed);
+  return forced >= 0 ? forced : fs::fused_auto_config(B, D, V, packed, tiled);
 }
 
 // Shared body of fs_sample / fs_sample_partial / fs_sample_partial_lse
@@ -255,6 +255,103 @@ fs_status run_fused(const void* h, const void* W, int32_t B, int32_t D, int32_t 
   if (getenv("FS_LOG"))
     fprintf(stderr, "[flashsample] %s B=%d D=%d V=%d config=%s splits=%d\n", who, B, D, V,
             config_label(cfg), a.S);
+  return FS_OK;
+}
+
+// ---- grouped sampler in one launch ----
+// Most vocabulary blocks a grouped launch over G groups can have: each group's
+// blocks (at least 16 rows) start up to 3 rows before its first row.
+size_t max_splits_groups(int32_t V, int32_t G) {
+  return (static_cast<size_t>(V) + 18 * static_cast<size_t>(G)) / fs::kMinRowsPerBlock + 1;
+}
+
+size_t groups_workspace(int32_t B, int32_t V, int32_t G) {
+  return 3 * fs::round_up(sizeof(float) * B * max_splits_groups(V, G), 256);
+}
+
+// Shared body of fs_sample_groups_lse / fs_sample_groups_lse_packed.
+fs_status run_groups(const void* h, const void* W, int32_t B, int32_t D, int32_t V,
+                     int32_t vocab_offset, const float* temperature, uint64_t seed, uint64_t step,
+                     const int32_t* cuts, int32_t G, float* partial_val, int32_t* partial_idx,
+                     float* partial_lse, void* workspace, size_t workspace_bytes, void* stream,
+                     bool packed, const char* who) {
+  fs_status s = check_sample_args(h, W, B, D, V, vocab_offset, temperature, partial_idx,
+                                  partial_val, workspace);
+  if (s != FS_OK) return s;
+  if (!cuts) return fail(FS_ERR_INVALID_ARG, "%s: null cuts", who);
+  if (G < 1 || G > fs::kMaxGroups)
+    return fail(FS_ERR_INVALID_ARG, "%s: n_groups must be in [1, %d] (got %d)", who, fs::kMaxGroups,
+                G);
+  if (cuts[0] != 0 || cuts[G] != V)
+    return fail(FS_ERR_INVALID_ARG, "%s: cuts must start at 0 and end at V=%d (got %d .. %d)", who,
+                V, cuts[0], cuts[G]);
+  for (int32_t g = 0; g < G; ++g)
+    if (cuts[g + 1] <= cuts[g])
+      return fail(FS_ERR_INVALID_ARG, "%s: cuts must increase strictly (cuts[%d]=%d, cuts[%d]=%d)",
+                  who, g, cuts[g], g + 1, cuts[g + 1]);
+  if (B == 0) return FS_OK;
+  if (!partial_lse) return fail(FS_ERR_INVALID_ARG, "null pointer argument");
+  if (!aligned(partial_lse, 4))
+    return fail(FS_ERR_INVALID_ARG, "%s: partial_lse must be 4-byte aligned", who);
+  if (packed) {
+    if (D % 32 != 0)
+      return fail(FS_ERR_INVALID_ARG, "%s: D must be a multiple of 32 (got %d)", who, D);
+    for (int32_t g = 1; g < G; ++g)
+      if (cuts[g] % 16 != 0)
+        return fail(FS_ERR_INVALID_ARG, "%s: group starts must be multiples of 16 (cuts[%d]=%d)",
+                    who, g, cuts[g]);
+  }
+  if (B > kMaxFusedB)
+    return fail(FS_ERR_UNSUPPORTED, "%s: B=%d exceeds the %d batch rows one call can take", who,
+                B, kMaxFusedB);
+  const size_t need = groups_workspace(B, V, G);
+  if (workspace_bytes < need)
+    return fail(FS_ERR_WORKSPACE, "%s: workspace of %zu bytes is below the %zu required", who,
+                workspace_bytes, need);
+  const int cfg = choose_config(B, D, V, packed, true);
+  if (!fs::fused_config_tiled(cfg))
+    return fail(FS_ERR_UNSUPPORTED,
+                "%s: configuration %s sweeps rows across the vocabulary; a grouped launch needs "
+                "blocks of contiguous rows", who, config_label(cfg));
+  if (!fs::fused_config_supports(cfg, B, D))
+    return fail(FS_ERR_UNSUPPORTED, "%s: forced configuration %s does not support B=%d, D=%d",
+                who, config_label(cfg), B, D);
+  if (packed && !fs::fused_config_reads_packed(cfg))
+    return fail(FS_ERR_UNSUPPORTED, "%s: configuration %s has no packed-W kernel", who,
+                config_label(cfg));
+  if (launch_fault_injected()) return injected_failure(who);
+  const size_t S = max_splits_groups(V, G);
+  const size_t region = fs::round_up(sizeof(float) * B * S, 256);
+  char* ws = static_cast<char*>(workspace);
+  fs::SampleArgs a;
+  a.h = static_cast<const __bf16*>(h);
+  a.W = static_cast<const __bf16*>(W);
+  a.B = B;
+  a.D = D;
+  a.V = V;
+  a.vocab_offset = vocab_offset;
+  a.temperature = temperature;
+  a.seed = seed;
+  a.step = step;
+  a.part_val = reinterpret_cast<float*>(ws);
+  a.part_idx = reinterpret_cast<int32_t*>(ws + region);
+  a.part_lse = reinterpret_cast<float*>(ws + 2 * region);
+  a.S = 0;
+  a.w_packed = packed;
+  a.n_groups = G;
+  for (int32_t g = 0; g <= G; ++g) a.grp_rows[g] = cuts[g];
+  const hipStream_t st = static_cast<hipStream_t>(stream);
+  hipError_t e = fs::launch_fused(cfg, a, st);
+  if (e != hipSuccess) return hip_fail(e, "fused sampler launch");
+  fs::GroupTiles gt;
+  gt.n = G;
+  for (int32_t g = 0; g <= G; ++g) gt.t[g] = a.grp_tiles[g];
+  e = fs::launch_merge_group_tiles_lse(a.part_val, a.part_idx, a.part_lse, a.S, B, gt, temperature,
+                                       partial_val, partial_idx, partial_lse, st);
+  if (e != hipSuccess) return hip_fail(e, "group merge launch");
+  if (getenv("FS_LOG"))
+    fprintf(stderr, "[flashsample] %s B=%d D=%d V=%d groups=%d config=%s splits=%d\n", who, B, D,
+            V, G, config_label(cfg), a.S);
   return FS_OK;
 }
 
@@ -513,6 +610,32 @@ fs_status fs_sample_partial_lse_packed(const void* h, const void* W_packed, int3
                    "fs_sample_partial_lse_packed", true);
 }
 
+size_t fs_groups_workspace_bytes(int32_t B, int32_t D, int32_t V, int32_t n_groups) {
+  if (check_shape(B, D, V, 0) != FS_OK || n_groups < 1 || n_groups > fs::kMaxGroups) return 0;
+  return groups_workspace(B, V, n_groups);
+}
+
+fs_status fs_sample_groups_lse(const void* h, const void* W, int32_t B, int32_t D, int32_t V,
+                               int32_t vocab_offset, const float* temperature, uint64_t seed,
+                               uint64_t step, const int32_t* cuts, int32_t n_groups,
+                               float* partial_val, int32_t* partial_idx, float* partial_lse,
+                               void* workspace, size_t workspace_bytes, void* stream) {
+  return run_groups(h, W, B, D, V, vocab_offset, temperature, seed, step, cuts, n_groups,
+                    partial_val, partial_idx, partial_lse, workspace, workspace_bytes, stream,
+                    false, "fs_sample_groups_lse");
+}
+
+fs_status fs_sample_groups_lse_packed(const void* h, const void* W_packed, int32_t B, int32_t D,
+                                      int32_t V, int32_t vocab_offset, const float* temperature,
+                                      uint64_t seed, uint64_t step, const int32_t* cuts,
+                                      int32_t n_groups, float* partial_val, int32_t* partial_idx,
+                                      float* partial_lse, void* workspace, size_t workspace_bytes,
+                                      void* stream) {
+  return run_groups(h, W_packed, B, D, V, vocab_offset, temperature, seed, step, cuts, n_groups,
+                    partial_val, partial_idx, partial_lse, workspace, workspace_bytes, stream, true,
+                    "fs_sample_groups_lse_packed");
+}
+
 fs_status fs_merge_lse(const float* partial_val, const int32_t* partial_idx,
                        const float* partial_lse, int32_t P, int32_t B,
                        const float* temperature, uint64_t seed, uint64_t step,
@@ -743,6 +866,11 @@ int32_t fs_selected_config(int32_t B, int32_t D, int32_t V) {
 int32_t fs_selected_config_packed(int32_t B, int32_t D, int32_t V) {
   if (check_shape(B, D, V, 0) != FS_OK) return -1;
   return choose_config(B, D, V, true);
+}
+
+int32_t fs_selected_config_groups(int32_t B, int32_t D, int32_t V, int32_t packed) {
+  if (check_shape(B, D, V, 0) != FS_OK) return -1;
+  return choose_config(B, D, V, packed != 0, true);
 }
 
 const char* fs_status_string(fs_status s) {

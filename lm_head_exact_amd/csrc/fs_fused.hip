@@ -64,6 +64,49 @@ __global__ __launch_bounds__(256) void merge_tiles_lse_kernel(
   }
 }
 
+// Grouped launch: one wave per (batch row, group) over the group's tile
+// partials (element (b, t) at b * S + t, group g's tiles [groups.t[g],
+// groups.t[g+1])), the argmax and log-sum-exp as merge_tiles_lse_kernel,
+// into slot g of the G x B part-major outputs.
+__global__ __launch_bounds__(256) void merge_group_tiles_lse_kernel(
+    const float* __restrict__ val, const int32_t* __restrict__ idx, const float* __restrict__ lse,
+    int32_t S, int32_t B, GroupTiles groups, const float* __restrict__ temperature,
+    float* out_val, int32_t* out_idx, float* out_lse) {
+  const int lane = threadIdx.x & (kWave - 1);
+  const int b = blockIdx.x * 4 + (threadIdx.x >> 6);
+  const int g = blockIdx.y;
+  if (b >= B) return;  // uniform per wave
+  // the group's tile range, read with constant indices only (see the fused kernel)
+  int t0 = 0, t1 = 0;
+#pragma unroll
+  for (int k = 0; k < kMaxGroups; ++k) {
+    if (k == g) {
+      t0 = groups.t[k];
+      t1 = groups.t[k + 1];
+    }
+  }
+  ArgMax m;
+  m.init();
+  LseAcc l;
+  l.init();
+  for (int t = t0 + lane; t < t1; t += kWave) {
+    const int64_t o = static_cast<int64_t>(b) * S + t;
+    m.push(val[o], idx[o]);
+    l.merge(lse[o], 1.0f);  // a tile's log-sum-exp L is the pair (L, 1)
+  }
+#pragma unroll
+  for (int mask = 32; mask >= 1; mask >>= 1) {
+    m.xor_reduce(mask);
+    l.xor_reduce(mask);
+  }
+  if (lane == 0) {
+    const int64_t o = static_cast<int64_t>(g) * B + b;
+    out_val[o] = m.v;
+    out_idx[o] = m.i;
+    out_lse[o] = l.value(row_is_greedy(temperature[b]));
+  }
+}
+
 // Grouped merge, one wave per batch row over P group partials (part-major,
 // element (p, b) at p * B + b).  The categorical distribution factorises as
 // P(i) = P(G) P(i | G) with P(G) proportional to exp(LSE_G): each group's
@@ -178,6 +221,10 @@ bool fused_config_reads_packed(int id) {
   return id >= 0 && id < num_fused_configs() && configs()[id].packed_w;
 }
 
+bool fused_config_tiled(int id) {
+  return id >= 0 && id < num_fused_configs() && configs()[id].tiled;
+}
+
 bool fused_config_supports(int id, int32_t B, int32_t D) {
   return id >= 0 && id < num_fused_configs() && configs()[id].supports(B, D);
 }
@@ -215,7 +262,7 @@ double one_per_cu_fill(int id, int32_t V) {
 }
 }  // namespace
 
-static int auto_config_shape(int32_t B, int32_t D, int32_t V, bool packed);
+static int auto_config_shape(int32_t B, int32_t D, int32_t V, bool packed, bool tiled);
 
 // The configuration with the same loop and tile shape but non-temporal W
 // loads (name + "_ntl1"), if there is one, else `id`.  On fragment-order W
@@ -235,12 +282,12 @@ static int non_temporal_twin(int id) {
   return id >= 0 && id < static_cast<int>(twin.size()) ? twin[id] : id;
 }
 
-int fused_auto_config(int32_t B, int32_t D, int32_t V, bool packed) {
-  const int id = auto_config_shape(B, D, V, packed);
+int fused_auto_config(int32_t B, int32_t D, int32_t V, bool packed, bool tiled) {
+  const int id = auto_config_shape(B, D, V, packed, tiled);
   return packed ? non_temporal_twin(id) : id;
 }
 
-static int auto_config_shape(int32_t B, int32_t D, int32_t V, bool packed) {
+static int auto_config_shape(int32_t B, int32_t D, int32_t V, bool packed, bool tiled) {
   static const int persist[] = {config_id("persist_nt1_nw8_ks16_p8"),
                                 config_id("persist_nt2_nw8_ks16_p8"),
                                 config_id("persist_nt1_nw8_ks32_p8")};
@@ -277,8 +324,10 @@ static int auto_config_shape(int32_t B, int32_t D, int32_t V, bool packed) {
   static const int lds_narrow = config_id("lds_mr2_nt8_nw4_kc64_p8_wb1_br4");
   static const int stream_small = config_id("stream_mr4_nt1_nw4_p4_ntl0");
   static const int stream_big = config_id("stream_mr2_nt4_nw4_p4_ntl0");
-  for (int id : packed ? persist_packed : persist)
-    if (fused_config_supports(id, B, D)) return id;
+  // (a grouped launch needs blocks of contiguous rows: no persistent kernel)
+  if (!tiled)
+    for (int id : packed ? persist_packed : persist)
+      if (fused_config_supports(id, B, D)) return id;
   // (the K-split loop reads row-major W only: packed W goes on to the DMA loop)
   if (!packed && B <= 8 && fused_config_supports(ksplit, B, D)) return ksplit;
   // DMA candidates per batch width, first choice first: 512-row blocks, else
@@ -349,6 +398,16 @@ hipError_t launch_merge_tiles_lse(const float* val, const int32_t* idx, const fl
   const dim3 grid((B + 3) / 4);
   merge_tiles_lse_kernel<<<grid, 256, 0, stream>>>(val, idx, lse, S, B, temperature, out_ids,
                                                    out_val, out_lse);
+  return hipGetLastError();
+}
+
+hipError_t launch_merge_group_tiles_lse(const float* val, const int32_t* idx, const float* lse,
+                                        int32_t S, int32_t B, const GroupTiles& groups,
+                                        const float* temperature, float* out_val,
+                                        int32_t* out_idx, float* out_lse, hipStream_t stream) {
+  const dim3 grid((B + 3) / 4, groups.n);
+  merge_group_tiles_lse_kernel<<<grid, 256, 0, stream>>>(val, idx, lse, S, B, groups, temperature,
+                                                         out_val, out_idx, out_lse);
   return hipGetLastError();
 }
 

@@ -8,6 +8,9 @@
 
 namespace fs {
 
+// Most vocabulary groups one grouped launch takes (fs_sample_groups_lse).
+constexpr int kMaxGroups = 64;
+
 struct SampleArgs {
   const __bf16* h;
   const __bf16* W;
@@ -23,6 +26,15 @@ struct SampleArgs {
   const int32_t* live = nullptr;
   // W in fragment order (fs_pack_weights) instead of row-major [V][D]
   bool w_packed = false;
+  // Vocabulary groups of one grouped launch: group g holds W rows
+  // [grp_rows[g], grp_rows[g+1]) and vocabulary blocks [grp_tiles[g],
+  // grp_tiles[g+1]).  Each group's block grid starts at its own first row
+  // (shifted down to a global id divisible by 4), so no block holds rows of
+  // two groups.  n_groups == 0: one slice, the whole of W.  The launcher fills
+  // grp_tiles from grp_rows.
+  int32_t n_groups = 0;
+  int32_t grp_rows[kMaxGroups + 1];
+  int32_t grp_tiles[kMaxGroups + 1];
 };
 
 // One fused-sampler configuration (a main-loop policy and its tile shape).
@@ -33,6 +45,7 @@ struct FusedConfig {
   bool (*supports)(int32_t B, int32_t D);
   int order;  // configurations of equal order sum the contraction identically
   bool packed_w;  // can read W in fragment order
+  bool tiled;     // each block covers one contiguous block of rows (grouped launches)
 };
 
 // Configuration lists of the translation units fs_configs_*.hip.
@@ -46,8 +59,12 @@ int fused_configs_dma_ntl(const FusedConfig** out);
 int num_fused_configs();
 const char* fused_config_name(int id);
 int fused_rows_per_block(int id);
-// Automatic choice; `packed`: for W in fragment order (fs_pack_weights).
-int fused_auto_config(int32_t B, int32_t D, int32_t V, bool packed = false);
+// Automatic choice; `packed`: for W in fragment order (fs_pack_weights);
+// `tiled`: only configurations whose blocks each cover one contiguous block
+// of vocabulary rows (not the persistent kernels), as a grouped launch needs.
+int fused_auto_config(int32_t B, int32_t D, int32_t V, bool packed = false, bool tiled = false);
+// Whether configuration `id` can run a grouped launch.
+bool fused_config_tiled(int id);
 bool fused_config_supports(int id, int32_t B, int32_t D);
 bool fused_config_reads_packed(int id);
 // Configurations with equal order sum each logit's products identically.
@@ -68,6 +85,17 @@ hipError_t launch_merge_tiles_lse(const float* val, const int32_t* idx, const fl
                                   int32_t S, int32_t B, const float* temperature,
                                   int32_t* out_ids, float* out_val, float* out_lse,
                                   hipStream_t stream);
+// Per-group argmax and log-sum-exp of a grouped launch's tile partials
+// (element (b, t) at b * S + t; group g holds tiles [grp_tiles[g],
+// grp_tiles[g+1])) into slot g of G x B part-major outputs.
+struct GroupTiles {
+  int32_t n;
+  int32_t t[kMaxGroups + 1];
+};
+hipError_t launch_merge_group_tiles_lse(const float* val, const int32_t* idx, const float* lse,
+                                        int32_t S, int32_t B, const GroupTiles& groups,
+                                        const float* temperature, float* out_val,
+                                        int32_t* out_idx, float* out_lse, hipStream_t stream);
 // Grouped merge over P group partials, part-major (element (p, b) at p * B + b).
 hipError_t launch_merge_groups_lse(const float* val, const int32_t* idx, const float* lse,
                                    int32_t P, int32_t B, const float* temperature,

@@ -82,14 +82,32 @@ __attribute__((amdgpu_waves_per_eu(Loop::kWavesPerSimd))) void fused_sample_kern
   const int lane = threadIdx.x & (kWave - 1);
   const int wave = threadIdx.x >> 6;
   const int li = lane & 15, kb = lane >> 4;
-  // The vocabulary grid starts vocab_offset mod 4 rows before row 0, so that
-  // every lane's four consecutive rows begin at a global id divisible by 4.
-  const int shift = a.vocab_offset & 3;
   int tile, bblock;
   block_tile<Loop>(a, tile, bblock);
   if (tile >= a.S) return;  // padding block of a paired grid (block-uniform)
   if (a.live != nullptr && *a.live == 0) return;  // nothing left to sample (uniform)
-  const int row0 = Loop::row0(tile, wave) - shift;
+  // The block's vocabulary group in a grouped launch: its first row, its row
+  // count and its first block (the whole of W otherwise).  The table is read
+  // with constant indices only (a kernel-argument array indexed at run time
+  // could be copied to scratch memory); the scan is block-uniform.
+  int g_row0 = 0, g_rows = a.V, g_tile0 = 0;
+  if (a.n_groups > 0) {
+#pragma unroll
+    for (int k = 0; k < kMaxGroups; ++k) {
+      if (k < a.n_groups && a.grp_tiles[k] <= tile) {
+        g_row0 = a.grp_rows[k];
+        g_rows = a.grp_rows[k + 1] - a.grp_rows[k];
+        g_tile0 = a.grp_tiles[k];
+      }
+    }
+  }
+  // The group's block grid starts (vocab_offset + g_row0) mod 4 rows before its
+  // first row, so that every lane's four consecutive rows begin at a global id
+  // divisible by 4; fragment-order W is packed on the grid of the whole of W,
+  // shifted by vocab_offset mod 4.
+  const int shift = (a.vocab_offset + g_row0) & 3;
+  const int pack_shift = a.vocab_offset & 3;
+  const int row0 = g_row0 + Loop::row0(tile - g_tile0, wave) - shift;
   const int block_col0 = bblock * Loop::kBlockCols;
 
   const int col0 = block_col0 + Loop::col_off(wave);  // this wave's first batch row
@@ -107,7 +125,7 @@ __attribute__((amdgpu_waves_per_eu(Loop::kWavesPerSimd))) void fused_sample_kern
 
   f32x4 acc[MR][NT];
   if constexpr (PACKED)  // fragment-order W: groups of the unshifted grid
-    Loop::template run<true>(a.W, a.h, a.B, a.D, (a.V + shift + 15) / 16, row0 + shift,
+    Loop::template run<true>(a.W, a.h, a.B, a.D, (a.V + pack_shift + 15) / 16, row0 + pack_shift,
                              block_col0, acc, dyn_smem);
   else
     Loop::run(a.W, a.h, a.B, a.D, a.V, row0, block_col0, acc, dyn_smem);
@@ -115,7 +133,8 @@ __attribute__((amdgpu_waves_per_eu(Loop::kWavesPerSimd))) void fused_sample_kern
 
   // ---- epilogue: scale, perturb, running (max, argmax) per batch row ----
   // Lane (li, kb) holds batch row col0 + 16n + li and vocabulary rows
-  // row0 + 16m + 4kb + r, r = 0..3: one Philox block when vocab_offset % 4 == 0.
+  // row0 + 16m + 4kb + r, r = 0..3: one Philox block (global ids from a
+  // multiple of 4); rows outside the block's group never win.
   // With a log-sum-exp output (grouped sampler) the same pass also keeps a
   // running log-sum-exp of the scaled logits per batch row.
   const Philox philox(a.seed);
@@ -133,7 +152,7 @@ __attribute__((amdgpu_waves_per_eu(Loop::kWavesPerSimd))) void fused_sample_kern
       static_for<MR>([&](auto m) FS_INLINE {
         if (Loop::owns(wave, m, n)) {
           const int v0 = row0 + m * 16 + 4 * kb;  // vocab_offset + v0 is a multiple of 4
-          push_four<LSE>(best[n], acc[m][n], v0, a.V,
+          push_four<LSE>(best[n], acc[m][n], v0 - g_row0, g_rows,
                                  static_cast<uint32_t>(a.vocab_offset + v0),
                                  static_cast<uint32_t>(b), a.step, greedy, inv_t, philox,
                                  &lacc[n]);
@@ -368,7 +387,17 @@ hipError_t launch_cfg(SampleArgs& a, hipStream_t stream) {
     }();
     if (attr != hipSuccess) return attr;
   }
-  a.S = (a.V + (a.vocab_offset & 3) + rows - 1) / rows;
+  if (a.n_groups > 0) {  // each group's blocks start at its own first row
+    a.grp_tiles[0] = 0;
+    for (int g = 0; g < a.n_groups; ++g) {
+      const int grows = a.grp_rows[g + 1] - a.grp_rows[g];
+      const int gshift = (a.vocab_offset + a.grp_rows[g]) & 3;
+      a.grp_tiles[g + 1] = a.grp_tiles[g] + (grows + gshift + rows - 1) / rows;
+    }
+    a.S = a.grp_tiles[a.n_groups];
+  } else {
+    a.S = (a.V + (a.vocab_offset & 3) + rows - 1) / rows;
+  }
   const int nb = batch_blocks<Loop>(a.B);
   // grid limits: x < 2^31 blocks, y <= 65535 (checked here, before launching)
   const int64_t paired_x = static_cast<int64_t>((a.S + kXcds - 1) / kXcds) * kXcds * nb;
@@ -451,7 +480,8 @@ struct Persist {
     return hipGetLastError();
   }
   static hipError_t launch(SampleArgs& a, hipStream_t stream) {
-    if (!supports(a.B, a.D)) return hipErrorInvalidValue;
+    // a block sweeps rows across the whole vocabulary: no grouped launches
+    if (!supports(a.B, a.D) || a.n_groups > 0) return hipErrorInvalidValue;
     if (a.w_packed) return a.part_lse == nullptr ? go<false, true>(a, stream) : go<true, true>(a, stream);
     return a.part_lse == nullptr ? go<false>(a, stream) : go<true>(a, stream);
   }
@@ -460,12 +490,12 @@ struct Persist {
 template <class Loop>
 constexpr FusedConfig make_cfg(const char* name, int order) {
   return {name, Loop::kRowsPerBlock, &launch_cfg<Loop>, &supports_cfg<Loop>, order,
-          reads_packed_w<Loop>::value};
+          reads_packed_w<Loop>::value, true};
 }
 
 template <class Pol>
 constexpr FusedConfig make_persist(const char* name, int order) {
-  return {name, 16, &Pol::launch, &Pol::supports, order, true};
+  return {name, 16, &Pol::launch, &Pol::supports, order, true, false};
 }
 
 #define FS_STREAM(MR, NT, NW, P, NTL) \

@@ -98,6 +98,16 @@ int main(void) {
                                       NULL), FS_ERR_UNSUPPORTED);
   expect("online packed cut", fs_sample_online_packed(A, A, 4, 256, 1000, 0, F, 1, 2, odd_cuts, 2, DB, I,
                                                       F, I, WS, big, NULL), FS_ERR_INVALID_ARG);
+  for (int packed = 0; packed <= 1; ++packed)
+    for (int i = 0; i < 7; ++i) (void)fs_selected_config_groups(Bs[i], 4096, 128256, packed);
+  expect("groups cuts", fs_sample_groups_lse(A, A, 4, 256, 1000, 0, F, 1, 2, bad_cuts, 2, F, I, F, WS, big,
+                                             NULL), FS_ERR_INVALID_ARG);
+  expect("groups n", fs_sample_groups_lse(A, A, 4, 256, 1000, 0, F, 1, 2, cuts, 65, F, I, F, WS, big, NULL),
+         FS_ERR_INVALID_ARG);
+  expect("groups packed cut", fs_sample_groups_lse_packed(A, A, 4, 256, 1000, 0, F, 1, 2, odd_cuts, 2, F, I,
+                                                          F, WS, big, NULL), FS_ERR_INVALID_ARG);
+  expect("groups ws", fs_sample_groups_lse(A, A, 4, 256, 1000, 0, F, 1, 2, cuts, 2, F, I, F, WS, 16, NULL),
+         FS_ERR_WORKSPACE);
   expect("noise n", fs_debug_noise(0, 0, 0, 0, -1, (uint32_t*)I, F, NULL), FS_ERR_INVALID_ARG);
   expect("noise range", fs_debug_noise(0, 0, 0, UINT32_MAX - 2, 5, (uint32_t*)I, F, NULL),
          FS_ERR_INVALID_ARG);
@@ -117,6 +127,10 @@ int main(void) {
          fs_sample_partial_lse(A, A, 4, 256, 1000, 0, F, 1, 2, F, I, F, WS, big, NULL), FS_ERR_HIP);
   expect("inj partial_lse_packed",
          fs_sample_partial_lse_packed(A, A, 4, 256, 1000, 0, F, 1, 2, F, I, F, WS, big, NULL), FS_ERR_HIP);
+  expect("inj groups", fs_sample_groups_lse(A, A, 4, 256, 1000, 0, F, 1, 2, cuts, 2, F, I, F, WS, big, NULL),
+         FS_ERR_HIP);
+  expect("inj groups packed", fs_sample_groups_lse_packed(A, A, 4, 256, 1000, 0, F, 1, 2, cuts, 2, F, I, F, WS,
+                                                          big, NULL), FS_ERR_HIP);
   expect("inj unfused", fs_sample_unfused(A, A, 4, 256, 1000, 0, F, 1, 2, I, F, WS, big, NULL), FS_ERR_HIP);
   expect("inj merge", fs_merge(F, I, 3, 4, I, F, NULL), FS_ERR_HIP);
   expect("inj merge_lse", fs_merge_lse(F, I, F, 3, 4, F, 1, 2, I, F, F, NULL), FS_ERR_HIP);

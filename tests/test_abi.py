@@ -355,6 +355,10 @@ def test_injected_launch_failure_every_entry_point(L, inject):
         "fs_online_bounds": lambda: L.fs_online_bounds(A, 1000, 256, cuts, 2, A, WS, big, None),
         "fs_sample_online": lambda: L.fs_sample_online(A, A, 4, 256, 1000, 0, A, 1, 2, cuts, 2,
                                                        A, A, A, A, WS, big, None),
+        "fs_sample_groups_lse": lambda: L.fs_sample_groups_lse(A, A, 4, 256, 1000, 0, A, 1, 2, cuts,
+                                                               2, A, A, A, WS, big, None),
+        "fs_sample_groups_lse_packed": lambda: L.fs_sample_groups_lse_packed(
+            A, A, 4, 256, 1000, 0, A, 1, 2, cuts, 2, A, A, A, WS, big, None),
         "fs_debug_noise": lambda: L.fs_debug_noise(0, 0, 0, 0, 16, A, A, None),
         "fs_debug_gumbel": lambda: L.fs_debug_gumbel(A, 16, A, None),
     }
@@ -404,3 +408,67 @@ def test_noalloc_argument_errors(L, kw, status):
         assert len(L.fs_last_error()) > 0
     if status == bd.FS_ERR_WORKSPACE:
         assert b"scratch" in L.fs_last_error()
+
+
+def _groups(L, fn="fs_sample_groups_lse", h=ALIGNED, W=ALIGNED, B=4, D=256, V=1000, off=0,
+            T=ALIGNED, cuts=(0, 512, 1000), n=None, val=ALIGNED, ids=ALIGNED, lse=ALIGNED,
+            ws=WS_ALIGNED, wsb=1 << 40):
+    c = (ctypes.c_int32 * len(cuts))(*cuts) if cuts is not None else None
+    n = len(cuts) - 1 if n is None else n
+    return getattr(L, fn)(h, W, B, D, V, off, T, 1, 2, c, n, val, ids, lse, ws, wsb, None)
+
+
+@pytest.mark.parametrize("kw,status", [
+    (dict(cuts=None, n=2), bd.FS_ERR_INVALID_ARG),
+    (dict(cuts=(0, 600, 600, 1000)), bd.FS_ERR_INVALID_ARG),         # empty group
+    (dict(cuts=(1, 500, 1000)), bd.FS_ERR_INVALID_ARG),              # does not start at 0
+    (dict(cuts=(0, 500, 999)), bd.FS_ERR_INVALID_ARG),               # does not end at V
+    (dict(n=0), bd.FS_ERR_INVALID_ARG),
+    (dict(cuts=tuple(range(0, 1001, 15)) + (1000,), n=None), bd.FS_ERR_INVALID_ARG),  # 67 groups
+    (dict(lse=None), bd.FS_ERR_INVALID_ARG),
+    (dict(lse=ALIGNED + 2), bd.FS_ERR_INVALID_ARG),
+    (dict(D=7), bd.FS_ERR_INVALID_ARG),
+    (dict(wsb=16), bd.FS_ERR_WORKSPACE),
+    (dict(fn="fs_sample_groups_lse_packed", cuts=(0, 500, 1000)), bd.FS_ERR_INVALID_ARG),
+    (dict(fn="fs_sample_groups_lse_packed", D=72, cuts=(0, 512, 1000)), bd.FS_ERR_INVALID_ARG),
+    (dict(B=0, h=None, W=None, T=None, val=None, ids=None, lse=None, ws=None), bd.FS_OK),
+])
+def test_groups_argument_errors(L, kw, status):
+    assert _groups(L, **kw) == status
+    if status != bd.FS_OK:
+        assert len(L.fs_last_error()) > 0
+
+
+def test_groups_refuse_a_forced_persistent_configuration(L):
+    names = [L.fs_config_name(i).decode() for i in range(L.fs_num_configs())]
+    persist = names.index("persist_nt1_nw8_ks16_p8")
+    assert L.fs_force_config(persist) == bd.FS_OK
+    try:
+        assert _groups(L, D=4096) == bd.FS_ERR_UNSUPPORTED
+        assert b"contiguous rows" in L.fs_last_error()
+    finally:
+        L.fs_force_config(-1)
+
+
+def test_groups_workspace_sizes(L):
+    assert L.fs_groups_workspace_bytes(4, 256, 1000, 0) == 0
+    assert L.fs_groups_workspace_bytes(4, 256, 1000, 65) == 0
+    need = L.fs_groups_workspace_bytes(4, 256, 1000, 2)
+    assert need >= L.fs_workspace_bytes(4, 256, 1000) and need % 256 == 0
+    assert _groups(L, wsb=need - 1) == bd.FS_ERR_WORKSPACE
+    assert _groups(L, wsb=need, ws=WS_ALIGNED + 4) == bd.FS_ERR_INVALID_ARG
+
+
+def test_groups_automatic_choice_is_tiled(L):
+    """The grouped launch's automatic choice never takes a persistent
+    configuration, and is fs_sample's choice wherever that one is tiled."""
+    assert L.fs_selected_config_groups(4, 7, 1000, 0) == -1
+    for packed in (0, 1):
+        for B in (1, 4, 8, 32, 64, 256, 512):
+            for D, V in ((4096, 128256), (8192, 16032), (256, 1000)):
+                c = L.fs_selected_config_groups(B, D, V, packed)
+                name = L.fs_config_name(c).decode()
+                assert not name.startswith("persist"), (B, D, V, packed, name)
+                plain = (L.fs_selected_config_packed if packed else L.fs_selected_config)(B, D, V)
+                if not L.fs_config_name(plain).decode().startswith("persist"):
+                    assert c == plain, (B, D, V, packed)

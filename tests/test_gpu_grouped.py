@@ -203,3 +203,133 @@ def test_partial_lse_full_workloads_sampled_rows(wlk, B):
     _check_lse(to_host(lse)[rows], o[3], f"{wlk.name} B={B}")
     del h, W
     torch.cuda.empty_cache()
+
+
+# ---------------------------------------------------------------------------
+# All groups in one launch (fs_sample_groups_lse)
+# ---------------------------------------------------------------------------
+GROUP_CASES = [
+    # (B, D, V, vocab_offset, cuts)
+    (24, 512, 9000, 0, [0, 1501, 3003, 5555, 7001, 9000]),        # uneven groups
+    (37, 256, 1531, 6, [0, 1, 17, 700, 1531]),                      # a one-row group
+    (300, 256, 2600, 3, [0, 1300, 2600]),                           # several batch blocks
+    (5, 4096, 3000, 1, [0, 1000, 2000, 3000]),                      # D = 4096, small batch
+]
+
+
+def _groups_separately(h, W, T, seed, step, off, cuts):
+    """Slot g by one fs_sample_partial_lse call over group g."""
+    B, G = h.shape[0], len(cuts) - 1
+    pv = torch.empty(G, B, dtype=torch.float32, device=DEV)
+    pi = torch.empty(G, B, dtype=torch.int32, device=DEV)
+    pl = torch.empty(G, B, dtype=torch.float32, device=DEV)
+    hd, Wd, Td = h.to(DEV), W.to(DEV), T.to(DEV)
+    for g, (a, c) in enumerate(zip(cuts[:-1], cuts[1:])):
+        fsl.sample_partial_lse(hd, Wd[a:c], Td, seed, step, off + a, pv[g], pi[g], pl[g])
+    torch.cuda.synchronize()
+    return to_host(pv), to_host(pi), to_host(pl)
+
+
+@pytest.mark.parametrize("cfg", range(_num_configs()))
+def test_groups_one_launch_every_tiled_config_equals_separate_calls(cfg):
+    """In one configuration the one-launch slots are the separate calls' bit
+    for bit (same blocks over each group, same summation order)."""
+    name = fsl.config_name(cfg)
+    fsl.force_config(cfg)
+    ran = 0
+    for B, D, V, off, cuts in GROUP_CASES:
+        h, W, T = _rand(B, D, V, seed=B + V)
+        try:
+            pv, pi, pl = fsl.sample_groups_lse(h.to(DEV), W.to(DEV), T.to(DEV), 13, 5, cuts, off)
+        except fsl.FlashSampleError as e:
+            assert e.status == fsl.binding.FS_ERR_UNSUPPORTED, (name, str(e))
+            continue
+        torch.cuda.synchronize()
+        sv, si, sl = _groups_separately(h, W, T, 13, 5, off, cuts)
+        pv, pi, pl = to_host(pv), to_host(pi), to_host(pl)
+        assert np.array_equal(pi, si), (name, B, D, V)
+        assert np.array_equal(pv.view(np.uint32), sv.view(np.uint32)), (name, B, D, V)
+        assert np.array_equal(pl.view(np.uint32), sl.view(np.uint32)), (name, B, D, V)
+        ran += 1
+    if name.startswith("persist"):
+        assert ran == 0, "persistent configurations must refuse grouped launches"
+        pytest.skip("persistent configuration: grouped launches refused as documented")
+    if ran == 0:
+        pytest.skip("configuration supports none of the test shapes")
+
+
+@pytest.mark.parametrize("case", range(len(GROUP_CASES)))
+def test_groups_one_launch_matches_oracle(case):
+    """The automatic choice, every group against oracle.sample_lse over its
+    slice on every row; then fs_merge_lse against the oracle merge."""
+    B, D, V, off, cuts = GROUP_CASES[case]
+    h, W, T = _rand(B, D, V, seed=3 * B + V)
+    hb, Wb, Tn = wl.bf16_bits(h), wl.bf16_bits(W), T.numpy()
+    pv, pi, pl = fsl.sample_groups_lse(h.to(DEV), W.to(DEV), T.to(DEV), 21, 2, cuts, off)
+    torch.cuda.synchronize()
+    o_val, o_ids, o_lse = [], [], []
+    for g, (a, c) in enumerate(zip(cuts[:-1], cuts[1:])):
+        check_rows(hb, Wb[a:c], Tn, 21, 2, off + a, to_host(pi[g]), to_host(pv[g]),
+                   label=f"one launch group {g}")
+        oi, ov, og, ol = oracle.sample_lse(hb, Wb[a:c], Tn, 21, 2, vocab_offset=off + a)
+        o_val.append(ov), o_ids.append(oi), o_lse.append(ol)
+    o_val, o_ids, o_lse = map(np.stack, (o_val, o_ids, o_lse))
+    _check_lse(to_host(pl).ravel(), o_lse.ravel(), "one-launch group partials")
+    g_id, g_val, g_lse = [to_host(x) for x in fsl.merge_lse(pv, pi, pl, T.to(DEV), 21, 2)]
+    m_id, m_val, m_lse, m_gap = oracle.merge_lse(o_val, o_ids, o_lse, Tn, 21, 2)
+    _check_lse(g_lse, m_lse, "one-launch total")
+    full = oracle.sample_lse(hb, Wb, Tn, 21, 2, vocab_offset=off)
+    _check_lse(g_lse, full[3], "one-launch total vs whole vocabulary")
+    ok = (g_id == m_id) | (m_gap <= KEY_TOL)
+    # remaining mismatches: the same group chosen, a near tie of its tokens
+    for b in np.nonzero(~ok)[0]:
+        p = int(np.searchsorted(cuts, m_id[b] - off, side="right")) - 1
+        assert int(np.searchsorted(cuts, g_id[b] - off, side="right")) - 1 == p, b
+        a, c = cuts[p], cuts[p + 1]
+        _, _, og, _ = oracle.sample_lse(hb, Wb[a:c], Tn, 21, 2, vocab_offset=off + a, rows=[b])
+        assert og[0] <= 2e-3, f"row {b}: gpu {g_id[b]} oracle {m_id[b]}"
+
+
+def test_groups_one_launch_packed_equals_row_major():
+    """Fragment-order W (group starts multiples of 16, unaligned offset): the
+    slots equal the row-major one-launch call's in the same configuration."""
+    B, D, V, off = 40, 512, 5000, 7
+    cuts = [0, 1024, 1040, 3200, V]
+    h, W, T = _rand(B, D, V, seed=77)
+    hd, Wd, Td = h.to(DEV), W.to(DEV), T.to(DEV)
+    Wp = fsl.pack_weights(Wd, off)
+    pk = fsl.sample_groups_lse(hd, Wp, Td, 4, 9, cuts, off, V=V)
+    fsl.force_config(fsl.selected_config(B, D, V, packed=True, tiled=True))
+    rm = fsl.sample_groups_lse(hd, Wd, Td, 4, 9, cuts, off)
+    torch.cuda.synchronize()
+    for a_, b_ in zip(pk, rm):
+        assert np.array_equal(to_host(a_).view(np.uint32), to_host(b_).view(np.uint32))
+    hb, Wb, Tn = wl.bf16_bits(h), wl.bf16_bits(W), T.numpy()
+    for g, (a, c) in enumerate(zip(cuts[:-1], cuts[1:])):
+        check_rows(hb, Wb[a:c], Tn, 4, 9, off + a, to_host(pk[1][g]), to_host(pk[0][g]),
+                   label=f"packed one launch group {g}")
+
+
+def test_groups_one_launch_full_size_eight_groups():
+    """Llama-3-8B-shaped head in 8 groups of 16032 rows at B = 256, the
+    configuration the bench times: sampled rows of every group against the
+    oracle, and the merged draw's total log-sum-exp against the oracle's
+    whole-vocabulary one."""
+    w, B = wl.LLAMA3_8B, 256
+    h = wl.make_h(w, B, DEV)
+    W = wl.make_w(w, DEV)
+    T = wl.make_temperature(w, B, DEV)
+    cuts = list(range(0, w.V + 1, w.V // 8))
+    seed, step = w.sampler_seed(3)
+    pv, pi, pl = fsl.sample_groups_lse(h, W, T, seed, step, cuts)
+    _, _, lse = fsl.merge_lse(pv, pi, pl, T, seed, step)
+    torch.cuda.synchronize()
+    hb, Wb, Tn = wl.bf16_bits(h), wl.bf16_bits(W), to_host(T)
+    rows = sample_rows(B, k=4, seed=8)
+    for g, (a, c) in enumerate(zip(cuts[:-1], cuts[1:])):
+        check_rows(hb, Wb[a:c], Tn, seed, step, a, to_host(pi[g]), to_host(pv[g]), rows=rows,
+                   label=f"8 groups, group {g}")
+    o = oracle.sample_lse(hb, Wb, Tn, seed, step, rows=rows)
+    _check_lse(to_host(lse)[rows], o[3], "8 groups total")
+    del h, W
+    torch.cuda.empty_cache()
