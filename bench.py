@@ -12,16 +12,20 @@ fs_sample on the row-major W, whose figures the line carries beside it
 ("row_major"; --no-packed makes row-major the headline).  The same line
 carries the B = 1 .. 256 sweep, the
 unfused baseline (logits and probabilities through device memory) timed the
-same way, the grouped (hierarchical) sampler over 1 and 8 vocabulary groups,
-the online sampler with early finalisation (8 vocabulary chunks), the packed
-(fragment-order) weight path beside each row-major figure, the
-Qwen3-shaped, large-batch and vocabulary-shard heads, the fused kernel's
-roofline fraction and the CPU oracle's rate.
+same way, the grouped (hierarchical) sampler over 1 and 8 vocabulary groups
+(all groups in one launch, and one launch per group), the online sampler with
+early finalisation (8 vocabulary chunks), the packed (fragment-order) weight
+path beside each row-major figure, the Qwen3-shaped, large-batch and
+vocabulary-shard heads, the fused kernel's roofline fraction and the CPU
+oracle's rate.  For context it also times the bf16 GEMM alone through
+torch.matmul (ROCm's BLAS library) at the headline batch, at B = 256 and on
+the large-batch head at B = 512.
 
 Prints ONE JSON line on stdout.  Usage:
   python bench.py [--gpus 1] [--steps K] [--warmup W] [--batch 32]
                   [--sweep 1,2,4,...] [--no-cpu-baseline] [--no-unfused]
                   [--no-grouped] [--no-online] [--no-packed] [--no-workloads]
+                  [--no-gemm-context]
                   [--profile-pass]
 --profile-pass runs a short fixed sequence for rocprofv3 (a few fused steps
 plus a 1 GiB device copy used to calibrate the HBM byte counters) and exits.
@@ -52,6 +56,7 @@ def parse():
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--no-unfused", action="store_true")
     ap.add_argument("--no-grouped", action="store_true")
+    ap.add_argument("--no-gemm-context", action="store_true")
     ap.add_argument("--no-workloads", action="store_true")
     ap.add_argument("--no-online", action="store_true")
     ap.add_argument("--no-packed", action="store_true")
@@ -72,7 +77,7 @@ def flops(B, D, V):
     return 2 * B * V * D
 
 
-TRAFFIC_PROFILE = os.path.join(ROOT, "profiles", "fused_sample_llama3_b32_hbm_traffic.txt")
+TRAFFIC_PROFILE = os.path.join(ROOT, "profiles", "fused_sample_llama3_b32_memory_counters.txt")
 
 
 def kernel_sources_sha256():
@@ -322,6 +327,20 @@ def main():
             del ukp
         sweep.append(entry)
         del kp
+    # Context, not a product path: the bf16 GEMM alone (B x V logits written to
+    # HBM in bf16, no sampling) through torch.matmul, i.e. ROCm's BLAS library,
+    # on the same row-major W.
+    gemm_only = []
+    for b in ((B, 256) if not args.no_gemm_context else ()):
+        h_c = wl.make_h(wlk, b, dev)
+        t = time_steps(torch, lambda i, h_c=h_c: torch.matmul(h_c, W.t()), 30, 5, stream) * 1e3
+        gemm_only.append({"B": b, "us_per_call": round(t, 2),
+                          "tflops": round(flops(b, D, V) / (t * 1e6), 1),
+                          "fused_step_us": next((e.get("packed_us_per_step", e["us_per_step"])
+                                                 for e in sweep if e["B"] == b), None)})
+        del h_c
+    torch.cuda.empty_cache()
+
     # Grouped (hierarchical) sampler: the vocabulary as G contiguous groups.
     # One step is fs_sample_groups_lse (every group's partials in one launch)
     # then fs_merge_lse; the same step as G fs_sample_partial_lse launches
@@ -493,6 +512,11 @@ def main():
                     e["packed_config"] = fsl.config_name(fsl.selected_config(b, wk.D, wk.V, packed=True))
                     e["packed_us_per_step"] = round(tp, 2)
                     e["packed_frac_of_roofline"] = round(roof / tp, 4)
+                if wk is wl.LARGE_BATCH and b == 512 and not args.no_gemm_context:
+                    tg = time_steps(torch, lambda i: torch.matmul(h_w, Ws[0].t()), 10, 3,
+                                    stream) * 1e3
+                    e["gemm_only_torch_matmul_us"] = round(tg, 2)
+                    torch.cuda.empty_cache()
                 workloads.append(e)
                 del h_w, T_w, out_w, ws_w
             del Ws, Wps
@@ -576,6 +600,7 @@ def main():
         "cpu_baseline": cpu,
         "sweep": sweep,
         "grouped_lse": grouped,
+        "gemm_only_torch_matmul": gemm_only,
         "online": online,
         "other_workloads": workloads,
         "device": {"name": props.name, "gcn_arch": getattr(props, "gcnArchName", ""),
