@@ -333,3 +333,40 @@ def test_groups_one_launch_full_size_eight_groups():
     _check_lse(to_host(lse)[rows], o[3], "8 groups total")
     del h, W
     torch.cuda.empty_cache()
+
+
+def test_groups_one_launch_sixty_four_groups():
+    """The largest group table (64 groups, among them one-row groups and
+    groups shorter than a block), row-major at an unaligned offset and in
+    fragment order: slots equal separate per-group calls bit for bit, and
+    every group meets the oracle on every row."""
+    B, D, V, off = 9, 256, 6000, 3
+    rng = np.random.default_rng(64)
+    inner = np.sort(rng.choice(np.arange(1, V), size=63, replace=False))
+    inner[:3] = [1, 2, 3]                                  # three one-row groups
+    cuts = [0] + sorted(set(int(x) for x in inner)) + [V]
+    assert len(cuts) == 65
+    h, W, T = _rand(B, D, V, seed=640)
+    hd, Wd, Td = h.to(DEV), W.to(DEV), T.to(DEV)
+    pv, pi, pl = fsl.sample_groups_lse(hd, Wd, Td, 8, 1, cuts, off)
+    cfg = fsl.selected_config(B, D, V, tiled=True)
+    fsl.force_config(cfg)
+    sv, si, sl = _groups_separately(h, W, T, 8, 1, off, cuts)
+    fsl.force_config(-1)
+    pv, pi, pl = to_host(pv), to_host(pi), to_host(pl)
+    assert np.array_equal(pi, si)
+    assert np.array_equal(pv.view(np.uint32), sv.view(np.uint32))
+    assert np.array_equal(pl.view(np.uint32), sl.view(np.uint32))
+    hb, Wb, Tn = wl.bf16_bits(h), wl.bf16_bits(W), T.numpy()
+    for g, (a, c) in enumerate(zip(cuts[:-1], cuts[1:])):
+        check_rows(hb, Wb[a:c], Tn, 8, 1, off + a, pi[g], pv[g], label=f"64 groups, group {g}")
+    # fragment order: group starts rounded to multiples of 16
+    pcuts = sorted(set([0] + [c - c % 16 for c in cuts[1:-1] if c >= 16] + [V]))
+    Wp = fsl.pack_weights(Wd, off)
+    qv, qi, ql = fsl.sample_groups_lse(hd, Wp, Td, 8, 1, pcuts, off, V=V)
+    fsl.force_config(fsl.selected_config(B, D, V, packed=True, tiled=True))
+    rv, ri, rl = fsl.sample_groups_lse(hd, Wd, Td, 8, 1, pcuts, off)
+    fsl.force_config(-1)
+    torch.cuda.synchronize()
+    for x, y in ((qv, rv), (qi, ri), (ql, rl)):
+        assert np.array_equal(to_host(x).view(np.uint32), to_host(y).view(np.uint32))
