@@ -53,6 +53,20 @@ fs_status injected_failure(const char* who) {
   return fail(FS_ERR_HIP, "%s: launch failure injected (FS_FAULT_INJECT=launch)", who);
 }
 
+// Called by every launching entry point once its arguments have passed the
+// checks, just before its first HIP call; true when a failure is to be
+// injected (and then no HIP call is made).  HIP keeps one pending error per
+// host thread: any failed runtime call sets it, and the next hipGetLastError()
+// returns and clears it.  The launchers read it right after each launch, so an
+// error left pending by an earlier call (the caller's, or one of this
+// library's that has already returned its own status) is discarded here
+// rather than reported again against this call's launches.
+bool start_launches() {
+  if (launch_fault_injected()) return true;
+  (void)hipGetLastError();
+  return false;
+}
+
 // Name of a configuration for messages (never a null pointer).
 const char* config_label(int cfg) {
   const char* n = fs::fused_config_name(cfg);
@@ -206,10 +220,10 @@ fs_status run_fused(const void* h, const void* W, int32_t B, int32_t D, int32_t 
       return fail(FS_ERR_WORKSPACE,
                   "%s: B=%d, V=%d needs %zu bytes of partials, beyond the %zu-byte scratch array",
                   who, B, V, need, kScratchBytes);
-    if (launch_fault_injected()) return injected_failure(who);
+    if (start_launches()) return injected_failure(who);
     const fs_status st = scratch_address(&workspace);
     if (st != FS_OK) return st;
-  } else if (launch_fault_injected()) {
+  } else if (start_launches()) {
     return injected_failure(who);
   }
   fs::SampleArgs a;
@@ -319,7 +333,7 @@ fs_status run_groups(const void* h, const void* W, int32_t B, int32_t D, int32_t
   if (packed && !fs::fused_config_reads_packed(cfg))
     return fail(FS_ERR_UNSUPPORTED, "%s: configuration %s has no packed-W kernel", who,
                 config_label(cfg));
-  if (launch_fault_injected()) return injected_failure(who);
+  if (start_launches()) return injected_failure(who);
   const size_t S = max_splits_groups(V, G);
   const size_t region = fs::round_up(sizeof(float) * B * S, 256);
   char* ws = static_cast<char*>(workspace);
@@ -431,7 +445,7 @@ static fs_status run_online(const void* h, const void* W, int32_t B, int32_t D, 
       return fail(FS_ERR_UNSUPPORTED, "%s: configuration %s has no packed-W kernel", who,
                   config_label(cfg));
   }
-  if (launch_fault_injected()) return injected_failure(who);
+  if (start_launches()) return injected_failure(who);
   const size_t S = max_splits(V);
   const size_t region = fs::round_up(sizeof(float) * B * S, 256);
   char* ws = static_cast<char*>(workspace);
@@ -496,7 +510,7 @@ static fs_status run_online_bounds(const void* W, int32_t V, int32_t D, int32_t 
   if (workspace_bytes < need)
     return fail(FS_ERR_WORKSPACE, "fs_online_bounds: workspace of %zu bytes is below the %zu required",
                 workspace_bytes, need);
-  if (launch_fault_injected()) return injected_failure("fs_online_bounds");
+  if (start_launches()) return injected_failure("fs_online_bounds");
   const hipStream_t st = static_cast<hipStream_t>(stream);
   double* norms = static_cast<double*>(workspace);
   double* chunk_max = reinterpret_cast<double*>(static_cast<char*>(workspace) +
@@ -554,7 +568,7 @@ fs_status fs_pack_weights(const void* W, int32_t V, int32_t D, int32_t vocab_off
   if (packed_bytes < need)
     return fail(FS_ERR_WORKSPACE, "fs_pack_weights: %zu bytes for W_packed, %zu required",
                 packed_bytes, need);
-  if (launch_fault_injected()) return injected_failure("fs_pack_weights");
+  if (start_launches()) return injected_failure("fs_pack_weights");
   hipError_t e = fs::launch_pack_weights(static_cast<const __bf16*>(W), V, D, vocab_offset,
                                          static_cast<__bf16*>(W_packed),
                                          static_cast<hipStream_t>(stream));
@@ -652,7 +666,7 @@ fs_status fs_merge_lse(const float* partial_val, const int32_t* partial_idx,
     return fail(FS_ERR_INVALID_ARG, "pointers must be 4-byte aligned");
   if (static_cast<int64_t>(P) * B > (int64_t{1} << 40))
     return fail(FS_ERR_INVALID_ARG, "P * B too large");
-  if (launch_fault_injected()) return injected_failure("fs_merge_lse");
+  if (start_launches()) return injected_failure("fs_merge_lse");
   hipError_t e = fs::launch_merge_groups_lse(partial_val, partial_idx, partial_lse, P, B,
                                              temperature, seed, step, out_ids, out_maxval,
                                              out_lse, static_cast<hipStream_t>(stream));
@@ -719,7 +733,7 @@ fs_status fs_merge(const float* partial_val, const int32_t* partial_idx, int32_t
     return fail(FS_ERR_INVALID_ARG, "pointers must be 4-byte aligned");
   if (static_cast<int64_t>(P) * B > (int64_t{1} << 40))
     return fail(FS_ERR_INVALID_ARG, "P * B too large");
-  if (launch_fault_injected()) return injected_failure("fs_merge");
+  if (start_launches()) return injected_failure("fs_merge");
   hipError_t e = fs::launch_merge(partial_val, partial_idx, P, B, B, 1, out_ids, out_maxval,
                                   static_cast<hipStream_t>(stream));
   if (e != hipSuccess) return hip_fail(e, "merge launch");
@@ -740,7 +754,7 @@ fs_status fs_sample_unfused(const void* h, const void* W, int32_t B, int32_t D, 
   if (workspace_bytes < need)
     return fail(FS_ERR_WORKSPACE, "fs_sample_unfused: workspace of %zu bytes is below the %zu required",
                 workspace_bytes, need);
-  if (launch_fault_injected()) return injected_failure("fs_sample_unfused");
+  if (start_launches()) return injected_failure("fs_sample_unfused");
   fs::SampleArgs a;
   a.h = static_cast<const __bf16*>(h);
   a.W = static_cast<const __bf16*>(W);
@@ -769,7 +783,7 @@ fs_status fs_debug_noise(uint64_t seed, uint64_t step, uint32_t row, uint32_t gv
   if (n == 0 || (!out_bits && !out_gumbel)) return FS_OK;
   if ((out_bits && !aligned(out_bits, 4)) || (out_gumbel && !aligned(out_gumbel, 4)))
     return fail(FS_ERR_INVALID_ARG, "outputs must be 4-byte aligned");
-  if (launch_fault_injected()) return injected_failure("fs_debug_noise");
+  if (start_launches()) return injected_failure("fs_debug_noise");
   hipError_t e = fs::launch_debug_noise(seed, step, row, gv0, n, out_bits, out_gumbel,
                                         static_cast<hipStream_t>(stream));
   if (e != hipSuccess) return hip_fail(e, "noise launch");
@@ -782,7 +796,7 @@ fs_status fs_debug_gumbel(const uint32_t* bits, int64_t n, float* out_gumbel, vo
   if (!bits || !out_gumbel) return fail(FS_ERR_INVALID_ARG, "null pointer argument");
   if (!aligned(bits, 4) || !aligned(out_gumbel, 4))
     return fail(FS_ERR_INVALID_ARG, "pointers must be 4-byte aligned");
-  if (launch_fault_injected()) return injected_failure("fs_debug_gumbel");
+  if (start_launches()) return injected_failure("fs_debug_gumbel");
   hipError_t e = fs::launch_debug_gumbel(bits, n, out_gumbel, static_cast<hipStream_t>(stream));
   if (e != hipSuccess) return hip_fail(e, "gumbel launch");
   return FS_OK;

@@ -138,6 +138,22 @@ def test_poisoned_workspace_and_repeat_runs():
     assert np.array_equal(ref[0], again[0]) and np.array_equal(ref[1], again[1])
 
 
+def test_error_left_pending_by_an_earlier_call_is_not_reported_again():
+    """A failed HIP runtime call leaves an error pending in the thread; the
+    next sampling call must neither fail on it nor change its result."""
+    import ctypes
+    h, W, T = _rand_inputs(24, 256, 3001, seed=31)
+    hd, Wd, Td = h.to(DEV), W.to(DEV), T.to(DEV)
+    ref = [to_host(x) for x in fsl.sample(hd, Wd, Td, 5, 6, vocab_offset=2)]
+    cus = ctypes.c_int32(0)
+    # device 1000 does not exist: the runtime refuses the query on the host
+    assert fsl.binding.lib().fs_device_info(1000, ctypes.byref(cus), None) == fsl.binding.FS_ERR_HIP
+    got = [to_host(x) for x in fsl.sample(hd, Wd, Td, 5, 6, vocab_offset=2)]
+    assert np.array_equal(ref[0], got[0]) and np.array_equal(ref[1], got[1])
+    check_rows(wl.bf16_bits(h), wl.bf16_bits(W), T.numpy(), 5, 6, 2, got[0], got[1],
+               label="after a failed runtime call")
+
+
 def _order_class(name):
     """Configurations that sum each logit's products in the same order: all
     single-wave-per-row loops, and D-sliced loops (K-split, persistent) with
