@@ -11,12 +11,13 @@ UndefinedBehaviorSanitizer (CPU only).
   FS_FAULT_INJECT=launch, valid ones -- nothing is launched.
 Any sanitizer report fails the run (halt on the first error).
 """
-import glob
 import os
 import shutil
 import subprocess
 
 import pytest
+
+from lm_head_exact_amd import build as lib_build
 
 ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
 HERE = os.path.join(ROOT, "tests", "sanitize")
@@ -52,8 +53,11 @@ def test_oracle_under_asan_and_ubsan(tmp_path):
 
 @pytest.mark.skipif(not (os.path.exists(HIPCC) and os.path.exists(CLANG)), reason="needs ROCm hipcc")
 def test_library_host_paths_under_asan_and_ubsan(tmp_path):
-    kernels = sorted(glob.glob(os.path.join(ROOT, "_build", "fs_configs_*.o")))
-    if not kernels:
+    # the configuration tables' objects of the current library build (by the
+    # build's own source list: stale objects of removed units are not linked)
+    kernels = [os.path.join(ROOT, "_build", os.path.splitext(src)[0] + ".o")
+               for src in lib_build.SOURCES if src.startswith("fs_configs_")]
+    if not kernels or not all(os.path.exists(k) for k in kernels):
         pytest.skip("kernel-table objects missing: run the library build first")
     flags = ["--offload-arch=gfx950", "-O1", "-g", "-std=c++17", "-fPIC", "-fvisibility=hidden",
              "-w", "-Xclang", "-target-feature", "-Xclang", "-packed-fp32-ops",
