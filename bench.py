@@ -396,7 +396,7 @@ def main():
             del graph
         plain = next((e.get("packed_us_per_step" if Wp is not None else "us_per_step")
                       for e in sweep if e["B"] == b), None)
-        cfg = fsl.selected_config(b, D, V, packed=Wp is not None, tiled=True)
+        cfg = fsl.selected_config(b, D, V, packed=Wp is not None, grouped=True)
         grouped.append({"B": b, "groups": G, "us_per_step": round(times["one_launch"], 2),
                         "per_group_launches_us_per_step": round(times["per_group_launches"], 2),
                         "config": fsl.config_name(cfg),

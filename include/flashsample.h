@@ -204,12 +204,13 @@ FS_API fs_status fs_sample_partial_lse_packed(const void* h, const void* W_packe
  * fs_merge_lse reads them) holds what fs_sample_partial_lse would return over
  * W rows [cuts[g], cuts[g+1]) at vocab_offset + cuts[g]: the group's
  * Gumbel-max (value, global id) and its log-sum-exp.  One fused launch covers
- * every group (each group's vocabulary blocks start at its own first row, so
- * no block mixes two groups) and one merge launch fills the slots, instead
- * of G launches each over a slice too short to fill the device.  It runs the
- * tiled kernel configurations only (a forced persistent configuration is
- * FS_ERR_UNSUPPORTED); within one summation order the slots equal the
- * separate calls bit for bit.
+ * every group (each group's vocabulary rows are tiled from its own first row,
+ * so no tile mixes two groups) and one merge launch fills the slots, instead
+ * of G launches each over a slice too short to fill the device.  In one
+ * configuration (fs_force_config) the slots' values and ids equal the
+ * separate calls bit for bit, and so do the log-sum-exps on the batch-tiled
+ * configurations; the persistent ones (small batches) add a group's
+ * log-sum-exp partials in another order, equal within rounding.
  *   workspace   >= fs_groups_workspace_bytes(B, D, V, G) bytes (0 for invalid
  *               arguments); contents on entry ignored
  * Errors as fs_sample_partial_lse; a cuts array that does not partition
@@ -356,8 +357,9 @@ FS_API const char* fs_config_name(int32_t id);
 FS_API fs_status fs_force_config(int32_t id);
 /* Configuration fs_sample would use for batch size B (after forcing), the
  * one fs_sample_packed would use, and the one fs_sample_groups_lse (packed
- * != 0: fs_sample_groups_lse_packed) would use over a V-row vocabulary.
- * -1 for an invalid shape. */
+ * != 0: fs_sample_groups_lse_packed) would use over a V-row vocabulary (the
+ * same choice as fs_sample's, or fs_sample_packed's).  -1 for an invalid
+ * shape. */
 FS_API int32_t fs_selected_config(int32_t B, int32_t D, int32_t V);
 FS_API int32_t fs_selected_config_packed(int32_t B, int32_t D, int32_t V);
 FS_API int32_t fs_selected_config_groups(int32_t B, int32_t D, int32_t V, int32_t packed);

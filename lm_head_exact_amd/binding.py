@@ -547,10 +547,10 @@ def force_config(i: int):
     _check(lib().fs_force_config(int(i)))
 
 
-def selected_config(B: int, D: int, V: int, packed: bool = False, tiled: bool = False) -> int:
-    """Configuration fs_sample (packed: fs_sample_packed) would use; tiled:
+def selected_config(B: int, D: int, V: int, packed: bool = False, grouped: bool = False) -> int:
+    """Configuration fs_sample (packed: fs_sample_packed) would use; grouped:
     the one fs_sample_groups_lse (or its packed form) would use."""
-    if tiled:
+    if grouped:
         return int(lib().fs_selected_config_groups(B, D, V, int(packed)))
     fn = lib().fs_selected_config_packed if packed else lib().fs_selected_config
     return int(fn(B, D, V))

@@ -3,6 +3,7 @@
 // Every argument is checked here, on the host, before any HIP call; kernels
 // assume the checked invariants (D % 8 == 0 and 16-byte aligned operands for
 // the 16-byte fragment loads, ids that fit in int32, enough workspace).
+#include <algorithm>
 #include <atomic>
 #include <cmath>
 #include <cstdarg>
@@ -174,9 +175,9 @@ void destroy_events() {
   g_prof.used = 0;
 }
 
-int choose_config(int32_t B, int32_t D, int32_t V, bool packed = false, bool tiled = false) {
+int choose_config(int32_t B, int32_t D, int32_t V, bool packed = false) {
   const int forced = g_forced_config.load(std::memory_order_relaxed);
-  return forced >= 0 ? forced : fs::fused_auto_config(B, D, V, packed, tiled);
+  return forced >= 0 ? forced : fs::fused_auto_config(B, D, V, packed);
 }
 
 // Shared body of fs_sample / fs_sample_partial / fs_sample_partial_lse
@@ -322,11 +323,7 @@ fs_status run_groups(const void* h, const void* W, int32_t B, int32_t D, int32_t
   if (workspace_bytes < need)
     return fail(FS_ERR_WORKSPACE, "%s: workspace of %zu bytes is below the %zu required", who,
                 workspace_bytes, need);
-  const int cfg = choose_config(B, D, V, packed, true);
-  if (!fs::fused_config_tiled(cfg))
-    return fail(FS_ERR_UNSUPPORTED,
-                "%s: configuration %s sweeps rows across the vocabulary; a grouped launch needs "
-                "blocks of contiguous rows", who, config_label(cfg));
+  const int cfg = choose_config(B, D, V, packed);
   if (!fs::fused_config_supports(cfg, B, D))
     return fail(FS_ERR_UNSUPPORTED, "%s: forced configuration %s does not support B=%d, D=%d",
                 who, config_label(cfg), B, D);
@@ -360,6 +357,9 @@ fs_status run_groups(const void* h, const void* W, int32_t B, int32_t D, int32_t
   fs::GroupTiles gt;
   gt.n = G;
   for (int32_t g = 0; g <= G; ++g) gt.t[g] = a.grp_tiles[g];
+  for (int32_t g = 0; g < G; ++g)
+    gt.end[g] = a.grp_span > 0 ? std::min(a.grp_tiles[g + 1], a.grp_tiles[g] + a.grp_span)
+                               : a.grp_tiles[g + 1];
   e = fs::launch_merge_group_tiles_lse(a.part_val, a.part_idx, a.part_lse, a.S, B, gt, temperature,
                                        partial_val, partial_idx, partial_lse, st);
   if (e != hipSuccess) return hip_fail(e, "group merge launch");
@@ -884,7 +884,7 @@ int32_t fs_selected_config_packed(int32_t B, int32_t D, int32_t V) {
 
 int32_t fs_selected_config_groups(int32_t B, int32_t D, int32_t V, int32_t packed) {
   if (check_shape(B, D, V, 0) != FS_OK) return -1;
-  return choose_config(B, D, V, packed != 0, true);
+  return choose_config(B, D, V, packed != 0);
 }
 
 const char* fs_status_string(fs_status s) {

@@ -64,9 +64,9 @@ __global__ __launch_bounds__(256) void merge_tiles_lse_kernel(
   }
 }
 
-// Grouped launch: one wave per (batch row, group) over the group's tile
-// partials (element (b, t) at b * S + t, group g's tiles [groups.t[g],
-// groups.t[g+1])), the argmax and log-sum-exp as merge_tiles_lse_kernel,
+// Grouped launch: one wave per (batch row, group) over the group's partials
+// (element (b, t) at b * S + t, group g's entries [groups.t[g],
+// groups.end[g])), the argmax and log-sum-exp as merge_tiles_lse_kernel,
 // into slot g of the G x B part-major outputs.
 __global__ __launch_bounds__(256) void merge_group_tiles_lse_kernel(
     const float* __restrict__ val, const int32_t* __restrict__ idx, const float* __restrict__ lse,
@@ -82,7 +82,7 @@ __global__ __launch_bounds__(256) void merge_group_tiles_lse_kernel(
   for (int k = 0; k < kMaxGroups; ++k) {
     if (k == g) {
       t0 = groups.t[k];
-      t1 = groups.t[k + 1];
+      t1 = groups.end[k];
     }
   }
   ArgMax m;
@@ -221,9 +221,6 @@ bool fused_config_reads_packed(int id) {
   return id >= 0 && id < num_fused_configs() && configs()[id].packed_w;
 }
 
-bool fused_config_tiled(int id) {
-  return id >= 0 && id < num_fused_configs() && configs()[id].tiled;
-}
 
 bool fused_config_supports(int id, int32_t B, int32_t D) {
   return id >= 0 && id < num_fused_configs() && configs()[id].supports(B, D);
@@ -262,7 +259,7 @@ double one_per_cu_fill(int id, int32_t V) {
 }
 }  // namespace
 
-static int auto_config_shape(int32_t B, int32_t D, int32_t V, bool packed, bool tiled);
+static int auto_config_shape(int32_t B, int32_t D, int32_t V, bool packed);
 
 // The configuration with the same loop and tile shape but non-temporal W
 // loads (name + "_ntl1"), if there is one, else `id`.  On fragment-order W
@@ -282,12 +279,12 @@ static int non_temporal_twin(int id) {
   return id >= 0 && id < static_cast<int>(twin.size()) ? twin[id] : id;
 }
 
-int fused_auto_config(int32_t B, int32_t D, int32_t V, bool packed, bool tiled) {
-  const int id = auto_config_shape(B, D, V, packed, tiled);
+int fused_auto_config(int32_t B, int32_t D, int32_t V, bool packed) {
+  const int id = auto_config_shape(B, D, V, packed);
   return packed ? non_temporal_twin(id) : id;
 }
 
-static int auto_config_shape(int32_t B, int32_t D, int32_t V, bool packed, bool tiled) {
+static int auto_config_shape(int32_t B, int32_t D, int32_t V, bool packed) {
   static const int persist[] = {config_id("persist_nt1_nw8_ks16_p8"),
                                 config_id("persist_nt2_nw8_ks16_p8"),
                                 config_id("persist_nt1_nw8_ks32_p8")};
@@ -324,10 +321,8 @@ static int auto_config_shape(int32_t B, int32_t D, int32_t V, bool packed, bool 
   static const int lds_narrow = config_id("lds_mr2_nt8_nw4_kc64_p8_wb1_br4");
   static const int stream_small = config_id("stream_mr4_nt1_nw4_p4_ntl0");
   static const int stream_big = config_id("stream_mr2_nt4_nw4_p4_ntl0");
-  // (a grouped launch needs blocks of contiguous rows: no persistent kernel)
-  if (!tiled)
-    for (int id : packed ? persist_packed : persist)
-      if (fused_config_supports(id, B, D)) return id;
+  for (int id : packed ? persist_packed : persist)
+    if (fused_config_supports(id, B, D)) return id;
   // (the K-split loop reads row-major W only: packed W goes on to the DMA loop)
   if (!packed && B <= 8 && fused_config_supports(ksplit, B, D)) return ksplit;
   // DMA candidates per batch width, first choice first: 512-row blocks, else

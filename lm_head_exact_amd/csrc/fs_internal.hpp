@@ -31,10 +31,14 @@ struct SampleArgs {
   // grp_tiles[g+1]).  Each group's block grid starts at its own first row
   // (shifted down to a global id divisible by 4), so no block holds rows of
   // two groups.  n_groups == 0: one slice, the whole of W.  The launcher fills
-  // grp_tiles from grp_rows.
+  // grp_tiles from grp_rows, and grp_span: group g's partials are entries
+  // [grp_tiles[g], grp_tiles[g+1]) of each row, or with grp_span > 0 (the
+  // persistent kernels, whose blocks sweep a group's 16-row groups) entries
+  // [grp_tiles[g], min(grp_tiles[g+1], grp_tiles[g] + grp_span)).
   int32_t n_groups = 0;
   int32_t grp_rows[kMaxGroups + 1];
   int32_t grp_tiles[kMaxGroups + 1];
+  int32_t grp_span = 0;
 };
 
 // One fused-sampler configuration (a main-loop policy and its tile shape).
@@ -45,7 +49,6 @@ struct FusedConfig {
   bool (*supports)(int32_t B, int32_t D);
   int order;  // configurations of equal order sum the contraction identically
   bool packed_w;  // can read W in fragment order
-  bool tiled;     // each block covers one contiguous block of rows (grouped launches)
 };
 
 // Configuration lists of the translation units fs_configs_*.hip.
@@ -60,11 +63,7 @@ int num_fused_configs();
 const char* fused_config_name(int id);
 int fused_rows_per_block(int id);
 // Automatic choice; `packed`: for W in fragment order (fs_pack_weights);
-// `tiled`: only configurations whose blocks each cover one contiguous block
-// of vocabulary rows (not the persistent kernels), as a grouped launch needs.
-int fused_auto_config(int32_t B, int32_t D, int32_t V, bool packed = false, bool tiled = false);
-// Whether configuration `id` can run a grouped launch.
-bool fused_config_tiled(int id);
+int fused_auto_config(int32_t B, int32_t D, int32_t V, bool packed = false);
 bool fused_config_supports(int id, int32_t B, int32_t D);
 bool fused_config_reads_packed(int id);
 // Configurations with equal order sum each logit's products identically.
@@ -88,9 +87,11 @@ hipError_t launch_merge_tiles_lse(const float* val, const int32_t* idx, const fl
 // Per-group argmax and log-sum-exp of a grouped launch's tile partials
 // (element (b, t) at b * S + t; group g holds tiles [grp_tiles[g],
 // grp_tiles[g+1])) into slot g of G x B part-major outputs.
+// Group g's partials in each row: entries [t[g], end[g]).
 struct GroupTiles {
   int32_t n;
   int32_t t[kMaxGroups + 1];
+  int32_t end[kMaxGroups];
 };
 hipError_t launch_merge_group_tiles_lse(const float* val, const int32_t* idx, const float* lse,
                                         int32_t S, int32_t B, const GroupTiles& groups,

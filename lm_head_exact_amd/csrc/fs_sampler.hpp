@@ -229,11 +229,22 @@ __attribute__((amdgpu_waves_per_eu(Loop::kWavesPerSimd))) void fused_sample_kern
 // fixed wave order) by one owner wave per batch tile, which runs the
 // epilogue; ownership rotates over the waves.  The running (max, argmax)
 // persists across groups, so a block emits one partial per batch row.
+//
+// GROUPED (a grouped launch, log-sum-exps included): the 16-row groups are
+// those of each vocabulary group's own grid (see SampleArgs), numbered
+// group after group, so a block meets the vocabulary groups in increasing
+// order.  The owner of batch tile n is fixed within a vocabulary group, so
+// the group's running pair sits in one wave, which writes it when the block
+// moves on: entry t of each row, t the block's first 16-row group in that
+// vocabulary group.  Vocabulary group g's partials are therefore entries
+// [grp_tiles[g], min(grp_tiles[g+1], grp_tiles[g] + grid size)).
 // Requires D == 32 * NW * KS.
 // ---------------------------------------------------------------------------
-template <int NT, int NW, int KS, int P, bool LSE, bool PACKED = false, bool NTL = false>
+template <int NT, int NW, int KS, int P, bool LSE, bool PACKED = false, bool NTL = false,
+          bool GROUPED = false>
 __global__ __launch_bounds__(NW * kWave) void persist_sample_kernel(SampleArgs a) {
   static_assert(KS % P == 0, "the load ring must tile a group");
+  static_assert(!GROUPED || LSE, "grouped launches carry log-sum-exps");
   extern __shared__ __attribute__((aligned(16))) unsigned char dyn_smem[];
   f32x4* red = reinterpret_cast<f32x4*>(dyn_smem);  // [2][NW][NT][kWave]
   if (a.live != nullptr && *a.live == 0) return;  // nothing left to sample (uniform)
@@ -244,8 +255,38 @@ __global__ __launch_bounds__(NW * kWave) void persist_sample_kernel(SampleArgs a
   const int kbeg = wave * KS * 32 + 8 * kb;
   // 16-row groups over a vocabulary grid shifted as in the tiled kernel
   const int shift = a.vocab_offset & 3;
-  const int ngroups = (a.V + shift + 15) / 16;
+  const int ngroups = GROUPED ? a.S : (a.V + shift + 15) / 16;
   const int G = gridDim.x;
+  // Grouped launch: the group table, copied once into LDS (entry k by thread
+  // k) and then read at the vocabulary group of a cursor that only moves
+  // forward, since a block's 16-row groups come in increasing order.
+  __shared__ int32_t s_grp_rows[GROUPED ? kMaxGroups + 1 : 1];
+  __shared__ int32_t s_grp_tiles[GROUPED ? kMaxGroups + 1 : 1];
+  if constexpr (GROUPED) {
+    const int k = static_cast<int>(threadIdx.x);
+    if (k <= a.n_groups) {
+      s_grp_rows[k] = a.grp_rows[k];
+      s_grp_tiles[k] = a.grp_tiles[k];
+    }
+    __syncthreads();
+  }
+  int cursor = 0;  // vocabulary group of the latest 16-row group looked up
+  // 16-row group t (non-decreasing from call to call): its first row (a row
+  // of W, negative before row 0) and, in a grouped launch, its vocabulary
+  // group (index, first row, row count).  t is block-uniform.
+  struct Rows { int row0, grp, g_row0, g_rows; };
+  auto rows_of = [&](int t) FS_INLINE {
+    const int tc = min(t, ngroups - 1);
+    Rows r{tc * 16 - shift, 0, 0, a.V};
+    if constexpr (GROUPED) {
+      while (cursor + 1 < a.n_groups && s_grp_tiles[cursor + 1] <= tc) ++cursor;
+      r.grp = cursor;
+      r.g_row0 = s_grp_rows[cursor];
+      r.g_rows = s_grp_rows[cursor + 1] - r.g_row0;
+      r.row0 = r.g_row0 - ((a.vocab_offset + r.g_row0) & 3) + 16 * (tc - s_grp_tiles[cursor]);
+    }
+    return r;
+  };
 
   bf16x8 hreg[KS][NT];
   bool bvalid[NT], greedy[NT];
@@ -260,14 +301,15 @@ __global__ __launch_bounds__(NW * kWave) void persist_sample_kernel(SampleArgs a
     inv_t[n] = row_inv_temperature(T);
   });
 
-  // PACKED: W in fragment order (packed_frag); group g is packed group g
+  // PACKED: W in fragment order (packed_frag): the 16 rows from row0 are
+  // packed group (row0 + shift) / 16 (vocabulary groups of a packed grouped
+  // launch start at multiples of 16, so their grids are the packed one)
   constexpr int kStep = PACKED ? kPackedStep : 32;  // elements between k-steps
-  auto group_ptr = [&](int g) FS_INLINE {
+  auto group_ptr = [&](const Rows& r) FS_INLINE {
     if constexpr (PACKED)
-      return packed_frag(a.W, min(g, ngroups - 1), D, lane) + wave * KS * kPackedStep;
+      return packed_frag(a.W, (r.row0 + shift) >> 4, D, lane) + wave * KS * kPackedStep;
     else
-      return a.W + static_cast<size_t>(clamp_row(min(g, ngroups - 1) * 16 + li - shift, a.V)) * D +
-             kbeg;
+      return a.W + static_cast<size_t>(clamp_row(r.row0 + li, a.V)) * D + kbeg;
   };
   const Philox philox(a.seed);
   ArgMax best[NT];
@@ -278,8 +320,30 @@ __global__ __launch_bounds__(NW * kWave) void persist_sample_kernel(SampleArgs a
   });
 
   int g = blockIdx.x;
-  const __bf16* ap = group_ptr(g);
-  const __bf16* ap_next = group_ptr(g + G);
+  Rows cur = rows_of(g), nxt = rows_of(g + G);
+  const __bf16* ap = group_ptr(cur);
+  const __bf16* ap_next = group_ptr(nxt);
+  // grouped launch: the vocabulary group whose pairs the block holds, and
+  // the entry they go to
+  int open_grp = -1, open_slot = 0;
+  auto flush_group = [&]() FS_INLINE {
+    static_for<NT>([&](auto n) FS_INLINE {
+      if ((n + open_grp) % NW == wave) {  // wave-uniform: the group's owner of tile n
+        best[n].xor_reduce(16);
+        best[n].xor_reduce(32);
+        lacc[n].xor_reduce(16);
+        lacc[n].xor_reduce(32);
+        if (kb == 0 && bvalid[n]) {
+          const size_t o = static_cast<size_t>(n * 16 + li) * a.S + open_slot;
+          a.part_val[o] = best[n].v;
+          a.part_idx[o] = best[n].i;
+          a.part_lse[o] = lacc[n].value(greedy[n]);
+        }
+        best[n].init();
+        lacc[n].init();
+      }
+    });
+  };
   bf16x8 ring[P];
   static_for<P>([&](auto p) FS_INLINE { ring[p] = load_frag<NTL>(ap + p * kStep); });
 
@@ -296,25 +360,42 @@ __global__ __launch_bounds__(NW * kWave) void persist_sample_kernel(SampleArgs a
       else
         ring[slot] = load_frag<NTL>(ap_next + (s + P - KS) * kStep);
     });
+    const Rows here = cur;
+    cur = nxt;
+    nxt = rows_of(g + 2 * G);
     ap = ap_next;
-    ap_next = group_ptr(g + 2 * G);
+    ap_next = group_ptr(nxt);
 
     const int par = it & 1;
     static_for<NT>([&](auto n) FS_INLINE {
       red[((par * NW + wave) * NT + n) * kWave + lane] = acc[n];
     });
     __syncthreads();
+    if constexpr (GROUPED) {
+      if (here.grp != open_grp) {  // block-uniform
+        if (open_grp >= 0) flush_group();
+        open_grp = here.grp;
+        open_slot = g;
+      }
+    }
+    // the owner of tile n rotates with the 16-row group (with the vocabulary
+    // group in a grouped launch)
+    const int turn = GROUPED ? here.grp : it;
     static_for<NT>([&](auto n) FS_INLINE {
-      if ((n + it) % NW == wave && bvalid[n]) {
+      if ((n + turn) % NW == wave && bvalid[n]) {
         f32x4 z = red[((par * NW + 0) * NT + n) * kWave + lane];
         for (int w = 1; w < NW; ++w) z += red[((par * NW + w) * NT + n) * kWave + lane];
         const int b = n * 16 + li;
-        const int v0 = g * 16 + 4 * kb - shift;  // ids grow with g for each owner
+        const int v0 = here.row0 + 4 * kb;  // ids grow with g for each owner
         const uint32_t gv0 = static_cast<uint32_t>(a.vocab_offset + v0);
-        push_four<LSE>(best[n], z, v0, a.V, gv0, static_cast<uint32_t>(b), a.step,
-                               greedy[n], inv_t[n], philox, &lacc[n]);
+        push_four<LSE>(best[n], z, v0 - here.g_row0, here.g_rows, gv0,
+                       static_cast<uint32_t>(b), a.step, greedy[n], inv_t[n], philox, &lacc[n]);
       }
     });
+  }
+  if constexpr (GROUPED) {
+    if (open_grp >= 0) flush_group();
+    return;
   }
 
   static_for<NT>([&](auto n) FS_INLINE {
@@ -395,6 +476,7 @@ hipError_t launch_cfg(SampleArgs& a, hipStream_t stream) {
       a.grp_tiles[g + 1] = a.grp_tiles[g] + (grows + gshift + rows - 1) / rows;
     }
     a.S = a.grp_tiles[a.n_groups];
+    a.grp_span = 0;
   } else {
     a.S = (a.V + (a.vocab_offset & 3) + rows - 1) / rows;
   }
@@ -479,9 +561,32 @@ struct Persist {
     kernel<<<a.S, NW * kWave, kSmemBytes, stream>>>(a);
     return hipGetLastError();
   }
+  // Grouped launch: every vocabulary group on its own grid of 16-row groups
+  // (its first row shifted down to a global id divisible by 4), numbered group
+  // after group; a.grp_span = the grid size that bounds each group's partials.
+  template <bool PACKED>
+  static hipError_t go_groups(SampleArgs& a, hipStream_t stream) {
+    const auto kernel = persist_sample_kernel<NT, NW, KS, P, true, PACKED, NTL, true>;
+    static OccupancyCache cache;
+    const int slots = resident_blocks(kernel, NW * kWave, kSmemBytes, cache);
+    if (slots <= 0) return hipErrorInvalidDevice;
+    a.grp_tiles[0] = 0;
+    for (int g = 0; g < a.n_groups; ++g) {
+      const int grows = a.grp_rows[g + 1] - a.grp_rows[g];
+      const int gshift = (a.vocab_offset + a.grp_rows[g]) & 3;
+      a.grp_tiles[g + 1] = a.grp_tiles[g] + (grows + gshift + 15) / 16;
+    }
+    a.S = a.grp_tiles[a.n_groups];
+    a.grp_span = a.S < slots ? a.S : slots;
+    kernel<<<a.grp_span, NW * kWave, kSmemBytes, stream>>>(a);
+    return hipGetLastError();
+  }
   static hipError_t launch(SampleArgs& a, hipStream_t stream) {
-    // a block sweeps rows across the whole vocabulary: no grouped launches
-    if (!supports(a.B, a.D) || a.n_groups > 0) return hipErrorInvalidValue;
+    if (!supports(a.B, a.D)) return hipErrorInvalidValue;
+    if (a.n_groups > 0) {  // grouped launches carry log-sum-exps
+      if (a.part_lse == nullptr) return hipErrorInvalidValue;
+      return a.w_packed ? go_groups<true>(a, stream) : go_groups<false>(a, stream);
+    }
     if (a.w_packed) return a.part_lse == nullptr ? go<false, true>(a, stream) : go<true, true>(a, stream);
     return a.part_lse == nullptr ? go<false>(a, stream) : go<true>(a, stream);
   }
@@ -490,12 +595,12 @@ struct Persist {
 template <class Loop>
 constexpr FusedConfig make_cfg(const char* name, int order) {
   return {name, Loop::kRowsPerBlock, &launch_cfg<Loop>, &supports_cfg<Loop>, order,
-          reads_packed_w<Loop>::value, true};
+          reads_packed_w<Loop>::value};
 }
 
 template <class Pol>
 constexpr FusedConfig make_persist(const char* name, int order) {
-  return {name, 16, &Pol::launch, &Pol::supports, order, true, false};
+  return {name, 16, &Pol::launch, &Pol::supports, order, true};
 }
 
 #define FS_STREAM(MR, NT, NW, P, NTL) \

@@ -439,13 +439,13 @@ def test_groups_argument_errors(L, kw, status):
         assert len(L.fs_last_error()) > 0
 
 
-def test_groups_refuse_a_forced_persistent_configuration(L):
+def test_groups_refuse_a_forced_configuration_that_does_not_fit(L):
     names = [L.fs_config_name(i).decode() for i in range(L.fs_num_configs())]
-    persist = names.index("persist_nt1_nw8_ks16_p8")
+    persist = names.index("persist_nt1_nw8_ks16_p8")   # needs D = 4096
     assert L.fs_force_config(persist) == bd.FS_OK
     try:
-        assert _groups(L, D=4096) == bd.FS_ERR_UNSUPPORTED
-        assert b"contiguous rows" in L.fs_last_error()
+        assert _groups(L, D=256) == bd.FS_ERR_UNSUPPORTED
+        assert b"does not support" in L.fs_last_error()
     finally:
         L.fs_force_config(-1)
 
@@ -459,16 +459,13 @@ def test_groups_workspace_sizes(L):
     assert _groups(L, wsb=need, ws=WS_ALIGNED + 4) == bd.FS_ERR_INVALID_ARG
 
 
-def test_groups_automatic_choice_is_tiled(L):
-    """The grouped launch's automatic choice never takes a persistent
-    configuration, and is fs_sample's choice wherever that one is tiled."""
+def test_groups_automatic_choice_is_the_plain_one(L):
+    """A grouped launch takes the configuration fs_sample (fs_sample_packed)
+    takes, persistent ones included."""
     assert L.fs_selected_config_groups(4, 7, 1000, 0) == -1
     for packed in (0, 1):
         for B in (1, 4, 8, 32, 64, 256, 512):
             for D, V in ((4096, 128256), (8192, 16032), (256, 1000)):
                 c = L.fs_selected_config_groups(B, D, V, packed)
-                name = L.fs_config_name(c).decode()
-                assert not name.startswith("persist"), (B, D, V, packed, name)
                 plain = (L.fs_selected_config_packed if packed else L.fs_selected_config)(B, D, V)
-                if not L.fs_config_name(plain).decode().startswith("persist"):
-                    assert c == plain, (B, D, V, packed)
+                assert c == plain, (B, D, V, packed)
