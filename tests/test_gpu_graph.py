@@ -91,3 +91,30 @@ def test_grouped_step_graph_replays_match_eager():
     with torch.cuda.graph(graph):
         step()
     _replay_and_check(graph, outs, refs)
+
+
+@pytest.mark.parametrize("B,D,V", [(16, 4096, 4000), (70, 256, 4000)])
+def test_grouped_one_launch_graph_replays_match_eager(B, D, V):
+    """fs_sample_groups_lse then fs_merge_lse in one captured graph, on the
+    persistent kernel (D = 4096, small batch) and on a batch-tiled one."""
+    cuts = [0, 999, 1000, 2600, V]
+    G = len(cuts) - 1
+    h, W, T = _inputs(B, D, V, seed=B + 5)
+    pv = torch.empty(G, B, device=DEV)
+    pi = torch.empty(G, B, dtype=torch.int32, device=DEV)
+    pl = torch.empty(G, B, device=DEV)
+    ws = fsl.alloc_workspace(fsl.groups_workspace_bytes(B, D, V, G), DEV)
+    outs = (torch.empty(B, dtype=torch.int32, device=DEV), torch.empty(B, device=DEV),
+            torch.empty(B, device=DEV))
+
+    def step():
+        fsl.sample_groups_lse(h, W, T, 31, 32, cuts, vocab_offset=3, out=(pv, pi, pl), workspace=ws)
+        fsl.merge_lse(pv, pi, pl, T, 31, 32, out=outs)
+
+    step()
+    torch.cuda.synchronize()
+    refs = [to_host(o).copy() for o in (*outs, pv, pi, pl)]
+    graph = torch.cuda.CUDAGraph()
+    with torch.cuda.graph(graph):
+        step()
+    _replay_and_check(graph, (*outs, pv, pi, pl), refs)
