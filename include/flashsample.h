@@ -37,14 +37,19 @@
  *   - stream is a hipStream_t (NULL = the default stream).  Calls are
  *     asynchronous and ordered on that stream; the caller keeps every buffer
  *     alive until the stream has reached the work.
- *   - Ownership: the caller owns all memory.  The library allocates nothing,
- *     keeps no pointer after returning and holds no state between calls
- *     other than a forced-configuration switch (fs_force_config).
+ *   - Ownership: the caller owns all memory.  The library allocates nothing
+ *     on the sampling path (the one device array it holds, for
+ *     fs_sample_packed_noalloc, is static) and keeps no pointer after
+ *     returning; between calls it holds only a forced-configuration switch
+ *     (fs_force_config), per-device caches of device facts and launch sizes,
+ *     and the profiling recorder (fs_profile_enable).
  *   - Errors: the return code is the only channel.  Arguments are checked on
  *     the host before any HIP call; a rejected call launches nothing and
  *     writes nothing.  FS_ERR_HIP carries the runtime's message in
- *     fs_last_error() (thread-local).  Device-resident values are not
- *     inspected: NaN or infinite entries in h or W give undefined ids.
+ *     fs_last_error() (thread-local).  An error that an earlier failed HIP
+ *     call left pending in the calling thread is discarded before a call's
+ *     first launch, so it is not reported again.  Device-resident values are
+ *     not inspected: NaN or infinite entries in h or W give undefined ids.
  *   - B == 0 is a no-op that returns FS_OK (pointers may then be NULL).
  *     The samplers take at most 1048560 (16 * 65535) batch rows per call and
  *     the unfused baseline at most 65535 (the launch grids' row limit);
