@@ -270,7 +270,19 @@ __global__ __launch_bounds__(NW * kWave) void persist_sample_kernel(SampleArgs a
     }
     __syncthreads();
   }
-  int cursor = 0;  // vocabulary group of the latest 16-row group looked up
+  // The cursor's vocabulary group: index, first row, row count, first
+  // 16-row group, and the next group's first 16-row group (the table entries
+  // are the same on every lane: read into scalar registers, and only when the
+  // cursor moves).
+  int cursor = 0, c_row0 = 0, c_rows = a.V, c_tile0 = 0, c_next = 0x7FFFFFFF;
+  auto load_cursor = [&]() FS_INLINE {
+    c_row0 = __builtin_amdgcn_readfirstlane(s_grp_rows[cursor]);
+    c_rows = __builtin_amdgcn_readfirstlane(s_grp_rows[cursor + 1]) - c_row0;
+    c_tile0 = __builtin_amdgcn_readfirstlane(s_grp_tiles[cursor]);
+    c_next = cursor + 1 < a.n_groups ? __builtin_amdgcn_readfirstlane(s_grp_tiles[cursor + 1])
+                                     : 0x7FFFFFFF;
+  };
+  if constexpr (GROUPED) load_cursor();
   // 16-row group t (non-decreasing from call to call): its first row (a row
   // of W, negative before row 0) and, in a grouped launch, its vocabulary
   // group (index, first row, row count).  t is block-uniform.
@@ -279,11 +291,14 @@ __global__ __launch_bounds__(NW * kWave) void persist_sample_kernel(SampleArgs a
     const int tc = min(t, ngroups - 1);
     Rows r{tc * 16 - shift, 0, 0, a.V};
     if constexpr (GROUPED) {
-      while (cursor + 1 < a.n_groups && s_grp_tiles[cursor + 1] <= tc) ++cursor;
+      while (tc >= c_next) {
+        ++cursor;
+        load_cursor();
+      }
       r.grp = cursor;
-      r.g_row0 = s_grp_rows[cursor];
-      r.g_rows = s_grp_rows[cursor + 1] - r.g_row0;
-      r.row0 = r.g_row0 - ((a.vocab_offset + r.g_row0) & 3) + 16 * (tc - s_grp_tiles[cursor]);
+      r.g_row0 = c_row0;
+      r.g_rows = c_rows;
+      r.row0 = c_row0 - ((a.vocab_offset + c_row0) & 3) + 16 * (tc - c_tile0);
     }
     return r;
   };
